@@ -1,0 +1,220 @@
+"""ctypes wrapper of the plain C oracle (oracle/oracle.c).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package.  The product path
+(``moe_routing_amd``) never imports it and never falls back to it.
+
+Every function takes and returns numpy arrays; bf16 tensors are uint16 arrays
+holding the bf16 bit patterns, FP8 tensors are uint8 arrays of E4M3 codes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+# Every fp32 operation in oracle.c must be one IEEE-rounded operation.
+GCC_CMD = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+           "-fPIC", "-shared", _SRC, "-o", _LIB, "-lm"]
+
+SOFTMAX, SIGMOID = 0, 1
+
+_lib = None
+
+
+def build() -> str:
+    """Compile liboracle.so from oracle.c (always recompiles)."""
+    subprocess.run(GCC_CMD, check=True)
+    return _LIB
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        _lib = _declare(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def _p(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _declare(L: ctypes.CDLL) -> ctypes.CDLL:
+    vp, i32, i64, f32, f64 = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                              ctypes.c_float, ctypes.c_double)
+    L.orc_route.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f64, vp, vp]
+    L.orc_route.restype = i32
+    L.orc_map.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]
+    L.orc_map.restype = i32
+    L.orc_expand.argtypes = [vp, i32, i32, i32, vp, i32, i64, vp, vp]
+    L.orc_expand.restype = i32
+    L.orc_quant_row.argtypes = [vp, i32, vp, vp]
+    L.orc_quant_row.restype = None
+    L.orc_standin.argtypes = [vp, vp, i64, i32, f32, vp]
+    L.orc_standin.restype = None
+    L.orc_reduce.argtypes = [vp, i64, vp, vp, i32, i32, i32, vp]
+    L.orc_reduce.restype = i32
+    for name in ("orc_e4m3_from_f32_n", "orc_bf16_from_f32_n", "orc_bf16_from_f64_n",
+                 "orc_sigmoid_f32_n", "orc_exp_f32_n"):
+        getattr(L, name).argtypes = [vp, i64, vp]
+        getattr(L, name).restype = None
+    L.orc_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+    L.orc_e4m3_to_f64.restype = f64
+    L.orc_route_key.argtypes = [f32, i32, vp, i32]
+    L.orc_route_key.restype = f32
+    return L
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# ---------------------------------------------------------------- codecs ----
+def e4m3_from_f32(v) -> np.ndarray:
+    v = _c(v, np.float32)
+    q = np.empty(v.shape, np.uint8)
+    lib().orc_e4m3_from_f32_n(_p(v), v.size, _p(q))
+    return q
+
+
+def e4m3_to_f64(q) -> np.ndarray:
+    q = _c(q, np.uint8)
+    f = lib().orc_e4m3_to_f64
+    table = np.array([f(c) for c in range(256)], np.float64)
+    return table[q]
+
+
+def bf16_from_f32(v) -> np.ndarray:
+    v = _c(v, np.float32)
+    h = np.empty(v.shape, np.uint16)
+    lib().orc_bf16_from_f32_n(_p(v), v.size, _p(h))
+    return h
+
+
+def bf16_from_f64(v) -> np.ndarray:
+    v = _c(v, np.float64)
+    h = np.empty(v.shape, np.uint16)
+    lib().orc_bf16_from_f64_n(_p(v), v.size, _p(h))
+    return h
+
+
+def bf16_to_f32(h) -> np.ndarray:
+    h = _c(h, np.uint16)
+    return (h.astype(np.uint32) << 16).view(np.float32)
+
+
+def sigmoid_f32(x) -> np.ndarray:
+    x = _c(x, np.float32)
+    s = np.empty(x.shape, np.float32)
+    lib().orc_sigmoid_f32_n(_p(x), x.size, _p(s))
+    return s
+
+
+def exp_f32(x) -> np.ndarray:
+    x = _c(x, np.float32)
+    s = np.empty(x.shape, np.float32)
+    lib().orc_exp_f32_n(_p(x), x.size, _p(s))
+    return s
+
+
+def route_keys(logits, score: int, bias=None) -> np.ndarray:
+    """Selection keys the oracle ranks on (fp32), shape of logits."""
+    logits = _c(logits, np.float32)
+    if score == SOFTMAX:
+        return logits.copy()
+    s = sigmoid_f32(logits)
+    if bias is not None:
+        s = (s + _c(bias, np.float32)).astype(np.float32)  # fp32 add, RN
+    return s
+
+
+# ----------------------------------------------------------------- steps ----
+def route(logits, bias, k: int, score: int, n_groups: int = 1, topk_groups: int = 1,
+          group_topn: int = 0, renormalize: int = 1, route_scale: float = 1.0):
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    b = None if bias is None else _c(bias, np.float32)
+    idx = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    rc = lib().orc_route(_p(logits), _p(b), T, E, k, score, n_groups, topk_groups,
+                         group_topn, renormalize, float(route_scale), _p(idx), _p(w))
+    if rc != 0:
+        raise ValueError("oracle route: unsupported arguments")
+    return idx, w
+
+
+def map_routes(topk_idx, E: int, lo: int = 0, hi: int | None = None, with_row_src=True):
+    topk_idx = _c(topk_idx, np.int32)
+    T, k = topk_idx.shape
+    hi = E if hi is None else hi
+    nl = hi - lo
+    counts = np.empty(nl, np.int32)
+    offsets = np.empty(nl + 1, np.int32)
+    pos = np.empty((T, k), np.int32)
+    row_src = np.full(T * k, -1, np.int32) if with_row_src else None
+    rc = lib().orc_map(_p(topk_idx), T, k, E, lo, hi, _p(counts), _p(offsets), _p(pos),
+                       _p(row_src))
+    if rc != 0:
+        raise ValueError("oracle map: unsupported arguments")
+    if with_row_src:
+        row_src = row_src[: int(offsets[-1])].copy()
+    return counts, offsets, pos, row_src
+
+
+def quant_row(x_row):
+    """1x128 E4M3 quantisation of one or more bf16 rows (uint16, (..., H))."""
+    x = _c(x_row, np.uint16)
+    H = x.shape[-1]
+    flat = x.reshape(-1, H)
+    q = np.empty(flat.shape, np.uint8)
+    sc = np.empty((flat.shape[0], H // 128), np.float32)
+    for i in range(flat.shape[0]):
+        lib().orc_quant_row(_p(flat[i]), H, _p(q[i]), _p(sc[i]))
+    return q.reshape(x.shape), sc.reshape(x.shape[:-1] + (H // 128,))
+
+
+def expand(x, pos, mode: int, rows_capacity: int):
+    x = _c(x, np.uint16)
+    pos = _c(pos, np.int32)
+    T, H = x.shape
+    k = pos.shape[1]
+    if mode == 0:
+        out = np.zeros((rows_capacity, H), np.uint16)
+        scales = None
+    else:
+        out = np.zeros((rows_capacity, H), np.uint8)
+        scales = np.zeros((rows_capacity, H // 128), np.float32)
+    rc = lib().orc_expand(_p(x), T, H, k, _p(pos), mode, rows_capacity, _p(out), _p(scales))
+    if rc != 0:
+        raise ValueError("oracle expand: unsupported arguments")
+    return out, scales
+
+
+def standin(xq, scales, mult: float = 0.5):
+    xq = _c(xq, np.uint8)
+    scales = _c(scales, np.float32)
+    R, H = xq.shape
+    y = np.empty((R, H), np.uint16)
+    lib().orc_standin(_p(xq), _p(scales), R, H, float(mult), _p(y))
+    return y
+
+
+def reduce(y, pos, w):
+    y = _c(y, np.uint16)
+    pos = _c(pos, np.int32)
+    w = _c(w, np.float32)
+    T, k = pos.shape
+    R, H = y.shape
+    out = np.empty((T, H), np.uint16)
+    rc = lib().orc_reduce(_p(y), R, _p(pos), _p(w), T, k, H, _p(out))
+    if rc != 0:
+        raise ValueError("oracle reduce: unsupported arguments")
+    return out
