@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE routing hot path on one MI355X.
+
+One step = the whole path over one batch of the DeepSeek-V3-shaped workload
+(T=8192 tokens, hidden H=7168, E=256 experts in 8 groups of 32, top-8):
+
+  tk_route         sigmoid scores + per-expert bias, top-2 group sums, top-4
+                   groups, top-8 experts, weights normalised * 2.5
+  tk_map           counts, offsets, stable positions (no mask: all local)
+  tk_expand_quant  1x128 FP8 E4M3 expand into 65536 expert-contiguous rows
+  tk_reduce        bf16 combine of 65536 expert-output rows, fp32 accumulate
+
+Inputs are synthetic (seeded normal logits, U(-0.1,0.1) bias, bf16 N(0,1)
+hidden states with 1 % outlier rows x50, bf16 N(0,1) expert outputs) and
+resident in HBM before the timed region.  The expert GEMMs are not part of
+the path: the reduce consumes a fixed expert-output tensor.
+
+Prints ONE JSON line: routed tokens/s (value), the pipeline's algorithmic
+HBM GB/s, per-kernel times from HIP events recorded on the launch stream, the
+roofline of the dominant kernel (the reduce) and the CPU oracle's rate.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+T, H, E, K = 8192, 7168, 256, 8
+R = T * K
+NB = H // 128
+PEAK_HBM_GBPS = 8000.0
+
+# Algorithmic bytes per launch (each token read once, each expanded row written
+# once, each expert-output row read once; workspace traffic excluded).
+BYTES = {
+    "route": T * E * 4 + E * 4 + T * K * (4 + 4),
+    "map": T * K * 4 + T * K * 4 + R * 4 + (2 * E + 1) * 4,
+    "expand": T * H * 2 + R * H + R * NB * 4 + T * K * 4,
+    "reduce": R * H * 2 + T * K * 8 + T * H * 2,
+}
+BYTES["total"] = sum(BYTES.values())
+WORKLOAD = (f"DeepSeek-V3 MoE routing hot path: T={T} H={H} E={E} (8 groups x 32) k={K}; "
+            "sigmoid+bias gating, top-4 groups, weights x2.5; stable map; "
+            "1x128 FP8 E4M3 expand; bf16 combine with fp32 accumulation")
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "reduce_v3_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("reduce.hip", "tk_internal.h"):
+        with open(os.path.join(ROOT, "moe_routing_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per reduce launch from committed rocprofv3 counter runs, or
+    None when absent or taken on a different reduce kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inputs) -> dict:
+    """The oracle, as it stands, on the full workload (one step), one thread."""
+    import numpy as np
+    import oracle
+    logits, bias, x, y, r = inputs
+    t0 = time.perf_counter()
+    idx, w = oracle.route(logits, bias, K, **r)
+    counts, offsets, pos, row_src = oracle.map_routes(idx, E)
+    t1 = time.perf_counter()
+    xq, sc = oracle.expand(x, pos, 1, R)
+    t2 = time.perf_counter()
+    out = oracle.reduce(y, pos, w.astype(np.float32))
+    t3 = time.perf_counter()
+    del xq, sc, out
+    secs = t3 - t0
+    return {"value": T / secs, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"one full step (T={T}) of route+map+expand(FP8)+reduce, single-threaded C "
+                      f"oracle; route+map {t1 - t0:.2f}s, expand {t2 - t1:.2f}s, "
+                      f"reduce {t3 - t2:.2f}s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip timing the CPU oracle")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the routing path is built and timed on a single "
+              "MI355X; runs on more than one GPU are not supported.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from __graft_entry__ import _ensure_built
+    _ensure_built()
+    import moe_routing_amd as tk
+    from moe_routing_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gate = synth.v3_gate(0)
+    r = gate["route"]
+    x_h = synth.v3_hidden(0)
+    y_h = synth.v3_expert_out(0, R, H)
+
+    def up(a, bf16=False):
+        t = torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if bf16 else a)).to(dev)
+        return t.view(torch.bfloat16) if bf16 else t
+
+    logits, bias = up(gate["logits"]), up(gate["bias"])
+    x, y = up(x_h, True), up(y_h, True)
+    opts = tk.RouteOpts(**r)
+    idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+    w = torch.empty((T, K), dtype=torch.float32, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    pos = torch.empty((T, K), dtype=torch.int32, device=dev)
+    row_src = torch.empty(R, dtype=torch.int32, device=dev)
+    ws = torch.empty(max(tk.tk_map_workspace_bytes(T, K, E), 4), dtype=torch.uint8, device=dev)
+    xq = torch.empty((R, H), dtype=torch.uint8, device=dev)
+    sc = torch.empty((R, NB), dtype=torch.float32, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+
+    steps = ("route", "map", "expand", "reduce")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        tk.tk_route(logits, bias, K, opts, idx, w)
+        if ev is not None:
+            ev[1].record()
+        tk.tk_map(idx, E, 0, E, counts, offsets, pos, row_src, ws)
+        if ev is not None:
+            ev[2].record()
+        tk.tk_expand_quant(x, pos, tk.TK_EXPAND_FP8_E4M3_1X128, R, xq, sc)
+        if ev is not None:
+            ev[3].record()
+        tk.tk_reduce(y, pos, w, out)
+        if ev is not None:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # events on torch's current stream, which is the stream every tk_* call
+    # above launches on
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    per = {s: [] for s in steps}
+    for e in evs:
+        for j, s in enumerate(steps):
+            per[s].append(e[j].elapsed_time(e[j + 1]))
+    kern_us = {s: 1e3 * float(np.mean(v)) for s, v in per.items()}
+    kern_med_us = {s: 1e3 * float(np.median(v)) for s, v in per.items()}
+
+    if args.calib_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    ms_per_step = total_ms / args.steps
+    value = T / (ms_per_step * 1e-3)
+    gbps = BYTES["total"] / (ms_per_step * 1e-3) / 1e9
+    red_s = kern_us["reduce"] * 1e-6
+    achieved = BYTES["reduce"] / red_s / 1e9
+    traffic = measured_traffic()
+    result = {
+        "metric": "routed tokens/s and achieved HBM GB/s (% of peak), T=8192 H=7168 E=256 k=8",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "T": T, "H": H, "E": E, "k": K, "n_groups": 8,
+                   "topk_groups": 4, "route_scale": 2.5, "global_batch": T,
+                   "io": "logits fp32, hidden bf16, dispatch E4M3 + fp32 scales, combine bf16",
+                   "parallelism": "single GPU"},
+        "hbm_gbps": round(gbps, 1),
+        "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
+        "algorithmic_bytes_per_step": BYTES["total"],
+        "kernel_us_mean": {s: round(v, 2) for s, v in kern_us.items()},
+        "kernel_us_median": {s: round(v, 2) for s, v in kern_med_us.items()},
+        "kernel_gbps": {s: round(BYTES[s] / (kern_us[s] * 1e-6) / 1e9, 1) for s in steps},
+        "wall_s_timed": round(wall, 4),
+        "roofline": {"kernel": "reduce_kernel<8>", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_launch": BYTES["reduce"]},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        inputs = (gate["logits"], gate["bias"], x_h, y_h, r)
+        result["cpu_baseline"] = cpu_baseline(inputs)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,233 @@
+/*
+ * tk.h -- C ABI of the MoE routing hot path for AMD Instinct MI355X (gfx950).
+ *
+ * Four stream-ordered steps of a DeepSeek-V3-style MoE layer's token routing:
+ *
+ *   tk_route         top-k expert gating and scoring        (logits -> idx, w)
+ *   tk_map           token-to-expert mapping                (idx -> counts,
+ *                                                            offsets, pos)
+ *   tk_expand_quant  expand into expert-contiguous rows,    (x -> rows [+ FP8
+ *                    optionally fused 1x128 FP8 E4M3 quant    scales])
+ *   tk_reduce        weighted combine back to tokens        (rows, w -> out)
+ *
+ * plus tk_expert_standin, a dequantise-and-scale harness kernel that stands in
+ * for the expert computation in end-to-end tests.
+ *
+ * The operations are the ones the pages list for TileKernels' moe/ module --
+ * "top-k gating, expert scoring, token-to-expert mapping, fused
+ * expand/reduce, tensor-parallel mask" ("刚刚！DeepSeek开源高性能GPU算子库
+ * TileKernels", item moe/; "剛剛，DeepSeek開始頻繁更新：Tile Kernels、DeepEP V2",
+ * feature list) -- with per-token FP8 quantisation from the quant/ module
+ * (same pages) fused into the expand, at the DeepSeek-V3 shape with FP8
+ * dispatch and BF16 combine ("剛剛，DeepSeek開始頻繁更新…", section 性能表現).
+ * The top-k order and tie rule follow the gating listing on "DeepSeek 的 GPU
+ * 内核帝国：从 TileLang DSL 到 Engram 条件记忆…", section 第三层：TileKernels,
+ * subsection "MoE TopK 门控".
+ *
+ * Conventions for every call:
+ *  - Pointers are device pointers owned by the caller (a HIP allocation, e.g.
+ *    a torch tensor's storage).  The library allocates nothing, keeps no state
+ *    between calls and never synchronises the host: every call enqueues
+ *    kernels on `stream` and returns.  Calls are thread-safe.
+ *  - Tensors are dense and row-major.  Pointers of vector-accessed tensors
+ *    (noted per argument) must be 16-byte aligned.
+ *  - Host-side argument checks run before anything is launched; a failed
+ *    check returns TK_ERR_ARG (or TK_ERR_UNSUPPORTED for valid arguments the
+ *    kernels do not implement) and launches nothing.  A HIP launch error
+ *    returns TK_ERR_DEVICE.  tk_last_error() then describes the failure.
+ *    The library never aborts or exits.
+ *  - T == 0 is a valid no-op for every call.
+ *  - Device data that breaks a call's contract (an expert id out of range, a
+ *    row index beyond the capacity) never causes an out-of-bounds access:
+ *    the affected route or row is skipped as documented per call.
+ */
+#ifndef TK_H
+#define TK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t tk_status;
+#define TK_OK 0
+#define TK_ERR_ARG (-1)          /* invalid arguments; nothing launched */
+#define TK_ERR_UNSUPPORTED (-2)  /* valid but not implemented; nothing launched */
+#define TK_ERR_DEVICE (-3)       /* HIP launch / runtime error */
+
+/* Limits of this implementation. */
+#define TK_MAX_EXPERTS 1024
+#define TK_MAX_TOPK 32
+
+/* Text of the last failure on the calling thread; owned by the library, valid
+ * until the next tk_* call on that thread.  "" when the last call succeeded. */
+const char* tk_last_error(void);
+
+/* ------------------------------------------------------------------ route */
+#define TK_SCORE_SOFTMAX 0
+#define TK_SCORE_SIGMOID 1
+
+typedef struct tk_route_opts {
+    int32_t score;        /* TK_SCORE_SOFTMAX or TK_SCORE_SIGMOID */
+    int32_t n_groups;     /* expert groups of E/n_groups consecutive experts;
+                             1 = no group limiting */
+    int32_t topk_groups;  /* groups kept per token (n_groups > 1) */
+    int32_t group_topn;   /* a group's score is the sum of its group_topn
+                             largest selection keys (n_groups > 1) */
+    int32_t renormalize;  /* 1: weights of the k chosen experts are normalised
+                             to sum to route_scale; 0: raw scores * scale */
+    float route_scale;    /* final multiplier of the weights */
+} tk_route_opts;
+
+/*
+ * tk_route -- top-k expert gating and scoring, one token per wavefront.
+ *
+ * Per token t (row t of logits):
+ *  1. selection key per expert e (fp32):
+ *       softmax: key = logit (softmax is increasing in the logit, so its top-k
+ *                is the top-k of the logits);
+ *       sigmoid: s = 1/(1+E(-x)) with a fixed fp32 evaluation of E(y) = e^y
+ *                (Cody-Waite reduction by ln 2 in two parts, degree-7 Taylor
+ *                polynomial in Horner form with fused multiply-adds, IEEE
+ *                division), key = s + bias[e] (bias optional, selection only);
+ *  2. if n_groups > 1: group score = fp32 sum (largest first) of the group's
+ *     group_topn largest keys; the topk_groups best groups (ties -> lower
+ *     group) stay eligible, the other groups' experts do not;
+ *  3. k rounds of argmax over the eligible experts: largest key first, ties
+ *     to the lower expert index (-0 == +0), each winner removed; round j
+ *     writes slot j (the listing's rounds of max + min-index argmax);
+ *  4. weights (fp32):
+ *       sigmoid: w_j = s_j / (s_0 + ... + s_{k-1}) * route_scale (unbiased
+ *                scores, sum in slot order), or s_j * route_scale;
+ *       softmax: w_j = e^(x_j - x_0) / sum_i e^(x_i - x_0) * route_scale over
+ *                the k chosen experts, or the softmax over all E experts
+ *                times route_scale when renormalize == 0.
+ *
+ * logits   device, fp32 (T, E), 4-byte aligned (16-byte aligned if E % 4 == 0
+ *          for vector loads)
+ * bias     device, fp32 (E) or NULL; sigmoid only
+ * T        tokens, >= 0
+ * E        experts, 1..TK_MAX_EXPERTS
+ * k        experts per token, 1..min(E, TK_MAX_TOPK)
+ * opts     host pointer; n_groups must divide E, topk_groups in 1..n_groups,
+ *          group_topn in 1..E/n_groups, topk_groups*E/n_groups >= k.  Group
+ *          limiting additionally needs E/n_groups to be a multiple of the
+ *          experts held per lane (ceil(E/64) rounded up to a power of two) and
+ *          the lanes per group a power of two, else TK_ERR_UNSUPPORTED.
+ * topk_idx device, int32 (T, k) out: chosen experts, descending key order
+ * topk_w   device, fp32 (T, k) out: weights, slot-aligned with topk_idx
+ */
+tk_status tk_route(const float* logits, const float* bias, int32_t T, int32_t E, int32_t k,
+                   const tk_route_opts* opts, int32_t* topk_idx, float* topk_w,
+                   hipStream_t stream);
+
+/* -------------------------------------------------------------------- map */
+/* Bytes of device workspace tk_map needs for T tokens, k slots and
+ * n_local = local_end - local_begin experts (0 for T == 0). */
+size_t tk_map_workspace_bytes(int32_t T, int32_t k, int32_t n_local);
+
+/*
+ * tk_map -- token-to-expert mapping with a local-expert mask.
+ *
+ * Route (t, j) is local when local_begin <= topk_idx[t,j] < local_end (the
+ * experts one expert-parallel rank owns; [0, E) keeps every route).  An
+ * expert id repeated within one token's row is routed only at its first
+ * occurrence; ids outside [0, E) are never local.
+ *   counts[e]   = number of local routes to expert local_begin + e
+ *   offsets     = exclusive prefix sum of counts, offsets[n_local] = R
+ *   pos[t,j]    = offsets[e] + number of tokens t' < t routed to e: rows are
+ *                 expert-contiguous and, within an expert, in token order
+ *                 (stable); -1 for a route that is not local
+ *   row_src[r]  = token of expanded row r, for r < R (optional)
+ * Not-local routes keep their weights (nothing is renormalised), so partial
+ * combines of different ranks add up to the full combine.  Bit-exact and
+ * deterministic: no result depends on the order of atomics.
+ *
+ * topk_idx  device, int32 (T, k)
+ * T, k      T >= 0, 1 <= k <= TK_MAX_TOPK
+ * E         total experts, 1..TK_MAX_EXPERTS; 0 <= local_begin < local_end <= E
+ * counts    device, int32 (n_local) out
+ * offsets   device, int32 (n_local + 1) out
+ * pos       device, int32 (T, k) out
+ * row_src   device, int32 (T * k) out, or NULL; entries r >= R are untouched
+ * workspace device, >= tk_map_workspace_bytes(T, k, n_local) bytes, 4-byte
+ *           aligned; scratch, contents on entry ignored
+ */
+tk_status tk_map(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
+                 int32_t local_begin, int32_t local_end, int32_t* counts, int32_t* offsets,
+                 int32_t* pos, int32_t* row_src, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream);
+
+/* ----------------------------------------------------------------- expand */
+#define TK_EXPAND_BF16 0            /* rows are bitwise copies of the token */
+#define TK_EXPAND_FP8_E4M3_1X128 1  /* rows are 1x128-block FP8 E4M3 codes */
+
+/*
+ * tk_expand_quant -- gather tokens into expert-contiguous rows.
+ *
+ * For every route with 0 <= pos[t,j] < rows_capacity, row pos[t,j] of `out`
+ * receives token t (routes outside that range are skipped).  Each token is
+ * read from HBM once and written to all its rows.
+ * TK_EXPAND_FP8_E4M3_1X128: per token and block b of 128 columns,
+ *   amax = max(max |x|, 1e-4), scale = RN32(amax / 448),
+ *   q = E4M3(RN32(x / scale)) -- OCP E4M3FN, round to nearest even, sign kept;
+ *   scales[row, b] = scale for every row of the token.
+ *
+ * x_bf16        device, bf16 (T, H), 16-byte aligned
+ * T, H, k       T >= 0; H > 0 with H % 8 == 0 (bf16) or H % 128 == 0 (FP8)
+ * pos           device, int32 (T, k) (as written by tk_map)
+ * mode          TK_EXPAND_BF16 or TK_EXPAND_FP8_E4M3_1X128
+ * out           device, (rows_capacity, H) of bf16 or E4M3 bytes, 16-byte aligned
+ * scales        device, fp32 (rows_capacity, H/128), FP8 mode only (else NULL)
+ * rows_capacity rows available in out (and scales), >= 0
+ */
+tk_status tk_expand_quant(const void* x_bf16, int32_t T, int32_t H, int32_t k,
+                          const int32_t* pos, int32_t mode, void* out, float* scales,
+                          int64_t rows_capacity, hipStream_t stream);
+
+/* ----------------------------------------------------------------- reduce */
+/*
+ * tk_reduce -- weighted combine of expert outputs back to tokens.
+ *
+ *   out[t, c] = bf16_RNE( fp32 fma chain over j = 0..k-1, in slot order, of
+ *               topk_w[t,j] * y[pos[t,j], c] ), starting from +0,
+ * skipping routes with pos < 0 or pos >= rows.  A token without such a route
+ * gets a row of +0.
+ *
+ * y_bf16  device, bf16 (rows, H), 16-byte aligned
+ * rows    rows in y, >= 0
+ * pos     device, int32 (T, k)
+ * topk_w  device, fp32 (T, k)
+ * T, k, H T >= 0; 1 <= k <= TK_MAX_TOPK; H > 0, H % 8 == 0
+ * out     device, bf16 (T, H) out, 16-byte aligned
+ */
+tk_status tk_reduce(const void* y_bf16, int64_t rows, const int32_t* pos, const float* topk_w,
+                    int32_t T, int32_t k, int32_t H, void* out_bf16, hipStream_t stream);
+
+/* -------------------------------------------------------- test harness */
+/*
+ * tk_expert_standin -- stand-in for the expert computation in end-to-end
+ * tests of one expert-parallel rank: dequantise each FP8 row and scale it,
+ *   y[r, c] = bf16_RNE( RN32( RN32(dec(xq[r, c]) * scales[r, c/128]) * mult ) )
+ * for r < *n_rows (read on the device, e.g. offsets + n_local from tk_map,
+ * clamped to rows_capacity).  Not part of the routing path.
+ *
+ * xq      device, E4M3 (rows_capacity, H), 16-byte aligned
+ * scales  device, fp32 (rows_capacity, H/128)
+ * n_rows  device, one int32
+ * H       H > 0, H % 128 == 0
+ * y_bf16  device, bf16 (rows_capacity, H) out, 16-byte aligned
+ */
+tk_status tk_expert_standin(const uint8_t* xq, const float* scales, const int32_t* n_rows,
+                            int64_t rows_capacity, int32_t H, float mult, void* y_bf16,
+                            hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TK_H */

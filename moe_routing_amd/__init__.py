@@ -1,0 +1,222 @@
+"""MI355X (gfx950) MoE routing hot path: thin ctypes binding of libtk.so.
+
+The functions below carry the names of the C entry points declared in
+include/tk.h and only marshal arguments: they check dtypes, devices and
+shapes of torch tensors, allocate outputs the caller did not pass, and hand
+raw device pointers plus torch's current HIP stream to the library.  Every
+step of the path runs in the library's HIP kernels; there is no fallback.
+
+    tk_route(logits, bias, k, opts)            -> (topk_idx, topk_w)
+    tk_map(topk_idx, E, local_begin, local_end) -> (counts, offsets, pos, row_src)
+    tk_expand_quant(x, pos, mode, rows_capacity) -> (out, scales)
+    tk_reduce(y, pos, topk_w)                  -> out
+    tk_expert_standin(xq, scales, n_rows, mult) -> y
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtk.so")
+
+TK_OK, TK_ERR_ARG, TK_ERR_UNSUPPORTED, TK_ERR_DEVICE = 0, -1, -2, -3
+TK_MAX_EXPERTS, TK_MAX_TOPK = 1024, 32
+TK_SCORE_SOFTMAX, TK_SCORE_SIGMOID = 0, 1
+TK_EXPAND_BF16, TK_EXPAND_FP8_E4M3_1X128 = 0, 1
+
+
+class TkError(RuntimeError):
+    """A tk_* call returned a non-zero status."""
+
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed with status {status}: {text}")
+        self.status = status
+
+
+class _RouteOpts(ctypes.Structure):
+    _fields_ = [("score", ctypes.c_int32), ("n_groups", ctypes.c_int32),
+                ("topk_groups", ctypes.c_int32), ("group_topn", ctypes.c_int32),
+                ("renormalize", ctypes.c_int32), ("route_scale", ctypes.c_float)]
+
+
+@dataclass
+class RouteOpts:
+    score: int = TK_SCORE_SOFTMAX
+    n_groups: int = 1
+    topk_groups: int = 1
+    group_topn: int = 0
+    renormalize: int = 1
+    route_scale: float = 1.0
+
+    def _c(self) -> _RouteOpts:
+        return _RouteOpts(self.score, self.n_groups, self.topk_groups, self.group_topn,
+                          self.renormalize, self.route_scale)
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load libtk.so (built in-tree by __graft_entry__.build()); fail loudly if absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                              "(hipcc --offload-arch=gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                 ctypes.c_float, ctypes.c_size_t)
+        L.tk_last_error.argtypes = []
+        L.tk_last_error.restype = ctypes.c_char_p
+        L.tk_route.argtypes = [vp, vp, i32, i32, i32, ctypes.POINTER(_RouteOpts), vp, vp, vp]
+        L.tk_route.restype = i32
+        L.tk_map_workspace_bytes.argtypes = [i32, i32, i32]
+        L.tk_map_workspace_bytes.restype = sz
+        L.tk_map.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+        L.tk_map.restype = i32
+        L.tk_expand_quant.argtypes = [vp, i32, i32, i32, vp, i32, vp, vp, i64, vp]
+        L.tk_expand_quant.restype = i32
+        L.tk_reduce.argtypes = [vp, i64, vp, vp, i32, i32, i32, vp, vp]
+        L.tk_reduce.restype = i32
+        L.tk_expert_standin.argtypes = [vp, vp, vp, i64, i32, f32, vp, vp]
+        L.tk_expert_standin.restype = i32
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != TK_OK:
+        raise TkError(fn, status, library().tk_last_error().decode())
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int | None = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+    return t
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def tk_route(logits: torch.Tensor, bias: torch.Tensor | None, k: int, opts: RouteOpts,
+             topk_idx: torch.Tensor | None = None, topk_w: torch.Tensor | None = None):
+    _dev(logits, "logits", torch.float32, 2)
+    T, E = logits.shape
+    if bias is not None:
+        _dev(bias, "bias", torch.float32, 1)
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _dev(topk_idx, "topk_idx", torch.int32)
+    _dev(topk_w, "topk_w", torch.float32)
+    c = opts._c()
+    _check("tk_route", library().tk_route(_ptr(logits), _ptr(bias), T, E, k, ctypes.byref(c),
+                                          _ptr(topk_idx), _ptr(topk_w), _stream(logits)))
+    return topk_idx, topk_w
+
+
+def tk_map_workspace_bytes(T: int, k: int, n_local: int) -> int:
+    return int(library().tk_map_workspace_bytes(T, k, n_local))
+
+
+def tk_map(topk_idx: torch.Tensor, E: int, local_begin: int = 0, local_end: int | None = None,
+           counts=None, offsets=None, pos=None, row_src=None, workspace=None,
+           want_row_src: bool = True):
+    _dev(topk_idx, "topk_idx", torch.int32, 2)
+    T, k = topk_idx.shape
+    local_end = E if local_end is None else local_end
+    nl = local_end - local_begin
+    dev = topk_idx.device
+    counts = torch.empty(max(nl, 0), dtype=torch.int32, device=dev) if counts is None else counts
+    offsets = torch.empty(max(nl, 0) + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
+    pos = torch.empty((T, k), dtype=torch.int32, device=dev) if pos is None else pos
+    if row_src is None and want_row_src:
+        row_src = torch.empty(T * k, dtype=torch.int32, device=dev)
+    need = tk_map_workspace_bytes(T, k, nl) if nl > 0 else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
+    for name, t in (("counts", counts), ("offsets", offsets), ("pos", pos)):
+        _dev(t, name, torch.int32)
+    if row_src is not None:
+        _dev(row_src, "row_src", torch.int32)
+    _dev(workspace, "workspace", torch.uint8)
+    _check("tk_map", library().tk_map(_ptr(topk_idx), T, k, E, local_begin, local_end,
+                                      _ptr(counts), _ptr(offsets), _ptr(pos), _ptr(row_src),
+                                      _ptr(workspace), workspace.numel(), _stream(topk_idx)))
+    return counts, offsets, pos, row_src
+
+
+def tk_expand_quant(x: torch.Tensor, pos: torch.Tensor, mode: int, rows_capacity: int,
+                    out: torch.Tensor | None = None, scales: torch.Tensor | None = None):
+    _dev(x, "x", torch.bfloat16, 2)
+    _dev(pos, "pos", torch.int32, 2)
+    T, H = x.shape
+    k = pos.shape[1]
+    if pos.shape[0] != T:
+        raise ValueError("pos must have one row per token")
+    dev = x.device
+    if mode == TK_EXPAND_FP8_E4M3_1X128:
+        if out is None:
+            out = torch.empty((rows_capacity, H), dtype=torch.uint8, device=dev)
+        if scales is None:
+            scales = torch.empty((rows_capacity, max(H // 128, 1)), dtype=torch.float32, device=dev)
+        _dev(out, "out", torch.uint8)
+        _dev(scales, "scales", torch.float32)
+    else:
+        if out is None:
+            out = torch.empty((rows_capacity, H), dtype=torch.bfloat16, device=dev)
+        _dev(out, "out", torch.bfloat16)
+    if out.numel() < rows_capacity * H:
+        raise ValueError("out holds fewer than rows_capacity rows")
+    _check("tk_expand_quant", library().tk_expand_quant(
+        _ptr(x), T, H, k, _ptr(pos), mode, _ptr(out), _ptr(scales), rows_capacity, _stream(x)))
+    return out, scales
+
+
+def tk_reduce(y: torch.Tensor, pos: torch.Tensor, topk_w: torch.Tensor,
+              out: torch.Tensor | None = None):
+    _dev(y, "y", torch.bfloat16, 2)
+    _dev(pos, "pos", torch.int32, 2)
+    _dev(topk_w, "topk_w", torch.float32, 2)
+    T, k = pos.shape
+    R, H = y.shape
+    if tuple(topk_w.shape) != (T, k):
+        raise ValueError("topk_w must match pos")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    _dev(out, "out", torch.bfloat16, 2)
+    _check("tk_reduce", library().tk_reduce(_ptr(y), R, _ptr(pos), _ptr(topk_w), T, k, H,
+                                            _ptr(out), _stream(y)))
+    return out
+
+
+def tk_expert_standin(xq: torch.Tensor, scales: torch.Tensor, n_rows: torch.Tensor,
+                      mult: float = 0.5, y: torch.Tensor | None = None):
+    _dev(xq, "xq", torch.uint8, 2)
+    _dev(scales, "scales", torch.float32, 2)
+    _dev(n_rows, "n_rows", torch.int32)
+    cap, H = xq.shape
+    if y is None:
+        y = torch.empty((cap, H), dtype=torch.bfloat16, device=xq.device)
+    _dev(y, "y", torch.bfloat16, 2)
+    _check("tk_expert_standin", library().tk_expert_standin(
+        _ptr(xq), _ptr(scales), _ptr(n_rows), cap, H, float(mult), _ptr(y), _stream(xq)))
+    return y

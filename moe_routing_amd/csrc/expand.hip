@@ -1,0 +1,251 @@
+// tk_expand_quant: expand tokens into expert-contiguous rows, optionally with
+// fused per-token 1x128 FP8 E4M3 quantisation ("fused expand" of TileKernels'
+// moe/ module and "per-token FP8" of its quant/ module, "刚刚！DeepSeek开源高性能
+// GPU算子库TileKernels", items moe/ and quant/; FP8 dispatch at the DeepSeek-V3
+// shape, "剛剛，DeepSeek開始頻繁更新：Tile Kernels、DeepEP V2", section 性能表現).
+// Also tk_expert_standin, the dequantise-and-scale harness kernel.
+//
+// Token-major: one wave per token, walking the row in 1024-column chunks.
+// Each lane reads 16 bf16 (two 16-byte loads), so every 8-lane group holds one
+// 128-column quantisation block; the block amax is a 3-step DPP butterfly
+// inside the group.  The token's k row indices are loaded once.  The token
+// is read once and its 16 code bytes per lane are stored to each of its k
+// rows (one 1 KiB contiguous segment per row per wave), so HBM traffic is
+// T*H*2 read + R*H written, not R*H*2 read.
+//
+// Quotient x/scale: Markstein's correction on the reciprocal,
+//   inv = RN(1/scale); q0 = RN(x*inv); r = fma(-q0, scale, x); q = fma(r, inv, q0)
+// (P. Markstein, IBM J. Res. Dev. 34(1), 1990), which equals the IEEE
+// quotient RN(x/scale) for every (x, scale) this kernel can see; the exhaustive
+// host test of the bf16 x / block-scale domain is tests/test_quotient_domain.py.
+// FP8 encoding: gfx950's v_cvt_pk_fp8_f32 (OCP E4M3FN, round to nearest even).
+#include "tk_internal.h"
+
+namespace {
+
+constexpr int kChunkFp8 = 1024;   // columns per unit, FP8 mode (16 per lane)
+constexpr int kChunkBf16 = 512;   // columns per unit, bf16 mode (8 per lane)
+
+__device__ __forceinline__ float quotient(float x, float scale, float inv)
+{
+    const float q0 = x * inv;
+    const float r = __builtin_fmaf(-q0, scale, x);
+    return __builtin_fmaf(r, inv, q0);
+}
+
+__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d)
+{
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return static_cast<uint32_t>(w);
+}
+
+// Rows of token t: rows[j] for j < k, -1 where the route is skipped.
+template <int KMAX>
+__device__ __forceinline__ void token_rows(const int32_t* __restrict__ pos, int t, int k,
+                                           int64_t cap, int64_t (&rows)[KMAX])
+{
+    const int32_t* p = pos + static_cast<size_t>(t) * k;
+    int32_t r[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) r[j] = (j < k) ? p[j] : -1;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) rows[j] = (r[j] >= 0 && r[j] < cap) ? r[j] : -1;
+}
+
+// One token per wave; K > 0 is a compile-time k, K == 0 a runtime k.
+template <int K>
+__global__ __launch_bounds__(tk::kBlock) void expand_fp8_kernel(
+    const uint16_t* __restrict__ x, int T, int H, int k_rt, const int32_t* __restrict__ pos,
+    uint8_t* __restrict__ out, float* __restrict__ scales, int64_t cap)
+{
+    constexpr int KMAX = K > 0 ? K : TK_MAX_TOPK;
+    const int k = K > 0 ? K : k_rt;
+    const int lane = threadIdx.x & (tk::kWave - 1);
+    const int t = blockIdx.x * tk::kWavesPerBlock + tk::uniform(threadIdx.x / tk::kWave);
+    if (t >= T) return;
+    const int nb = H / 128;
+    int64_t rows[KMAX];
+    token_rows<KMAX>(pos, t, k, cap, rows);
+    const uint16_t* xt = x + static_cast<size_t>(t) * H;
+    for (int col0 = 0; col0 < H; col0 += kChunkFp8) {
+        const int col = col0 + lane * 16;
+        const bool active = col < H;
+        uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
+        if (active) {
+            const uint4* src = reinterpret_cast<const uint4*>(xt + col);
+            a = src[0];
+            b = src[1];
+        }
+        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            v[2 * i] = tk::bf16_lo(w[i]);
+            v[2 * i + 1] = tk::bf16_hi(w[i]);
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+        amax = fmaxf(tk::max_run8(amax), 1e-4f);   // one 128-column block per 8 lanes
+        const float scale = amax / 448.0f;
+        const float inv = 1.0f / scale;
+        uint4 q;
+        q.x = pack_fp8x4(quotient(v[0], scale, inv), quotient(v[1], scale, inv),
+                         quotient(v[2], scale, inv), quotient(v[3], scale, inv));
+        q.y = pack_fp8x4(quotient(v[4], scale, inv), quotient(v[5], scale, inv),
+                         quotient(v[6], scale, inv), quotient(v[7], scale, inv));
+        q.z = pack_fp8x4(quotient(v[8], scale, inv), quotient(v[9], scale, inv),
+                         quotient(v[10], scale, inv), quotient(v[11], scale, inv));
+        q.w = pack_fp8x4(quotient(v[12], scale, inv), quotient(v[13], scale, inv),
+                         quotient(v[14], scale, inv), quotient(v[15], scale, inv));
+        if (active) {
+#pragma unroll
+            for (int j = 0; j < KMAX; ++j) {
+                if (rows[j] < 0) continue;
+                *reinterpret_cast<uint4*>(out + static_cast<size_t>(rows[j]) * H + col) = q;
+                if ((lane & 7) == 0) scales[static_cast<size_t>(rows[j]) * nb + col / 128] = scale;
+            }
+        }
+    }
+}
+
+template <int K>
+__global__ __launch_bounds__(tk::kBlock) void expand_bf16_kernel(
+    const uint16_t* __restrict__ x, int T, int H, int k_rt, const int32_t* __restrict__ pos,
+    uint16_t* __restrict__ out, int64_t cap)
+{
+    constexpr int KMAX = K > 0 ? K : TK_MAX_TOPK;
+    const int k = K > 0 ? K : k_rt;
+    const int lane = threadIdx.x & (tk::kWave - 1);
+    const int t = blockIdx.x * tk::kWavesPerBlock + tk::uniform(threadIdx.x / tk::kWave);
+    if (t >= T) return;
+    int64_t rows[KMAX];
+    token_rows<KMAX>(pos, t, k, cap, rows);
+    const uint16_t* xt = x + static_cast<size_t>(t) * H;
+    for (int col = lane * 8; col < H; col += kChunkBf16) {
+        const uint4 a = *reinterpret_cast<const uint4*>(xt + col);
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+            if (rows[j] >= 0) *reinterpret_cast<uint4*>(out + static_cast<size_t>(rows[j]) * H + col) = a;
+    }
+}
+
+__global__ __launch_bounds__(tk::kBlock) void standin_kernel(
+    const uint8_t* __restrict__ xq, const float* __restrict__ scales,
+    const int32_t* __restrict__ n_rows, int64_t cap, int H, float mult,
+    uint16_t* __restrict__ y, int chunks)
+{
+    const int lane = threadIdx.x & (tk::kWave - 1);
+    const int nb = H / 128;
+    int64_t rows = *n_rows;
+    rows = rows < 0 ? 0 : (rows > cap ? cap : rows);
+    const int64_t n_units = rows * chunks;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * tk::kWavesPerBlock;
+    for (int64_t u = static_cast<int64_t>(blockIdx.x) * tk::kWavesPerBlock +
+                     tk::uniform(threadIdx.x / tk::kWave);
+         u < n_units; u += stride) {
+        const int64_t r = u / chunks;
+        const int col = static_cast<int>(u - r * chunks) * kChunkFp8 + lane * 16;
+        if (col >= H) continue;
+        const uint4 q = *reinterpret_cast<const uint4*>(xq + static_cast<size_t>(r) * H + col);
+        const float sc = scales[static_cast<size_t>(r) * nb + col / 128];
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+        uint32_t o[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int wi = static_cast<int>(w[i]);
+            const float d0 = __builtin_amdgcn_cvt_f32_fp8(wi, 0);
+            const float d1 = __builtin_amdgcn_cvt_f32_fp8(wi, 1);
+            const float d2 = __builtin_amdgcn_cvt_f32_fp8(wi, 2);
+            const float d3 = __builtin_amdgcn_cvt_f32_fp8(wi, 3);
+            o[2 * i] = tk::pack_bf16x2((d0 * sc) * mult, (d1 * sc) * mult);
+            o[2 * i + 1] = tk::pack_bf16x2((d2 * sc) * mult, (d3 * sc) * mult);
+        }
+        uint4* dst = reinterpret_cast<uint4*>(y + static_cast<size_t>(r) * H + col);
+        dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+        dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+}
+
+// Workgroups for a grid-stride loop over n_units waves of work.
+unsigned grid_for(int64_t n_units)
+{
+    const int64_t blocks = (n_units + tk::kWavesPerBlock - 1) / tk::kWavesPerBlock;
+    constexpr int64_t kMaxBlocks = 1 << 16;
+    return static_cast<unsigned>(blocks < kMaxBlocks ? (blocks < 1 ? 1 : blocks) : kMaxBlocks);
+}
+
+}  // namespace
+
+TK_EXPORT tk_status tk_expand_quant(const void* x_bf16, int32_t T, int32_t H, int32_t k,
+                                    const int32_t* pos, int32_t mode, void* out, float* scales,
+                                    int64_t rows_capacity, hipStream_t stream)
+{
+    using tk::fail;
+    if (T < 0) return fail(TK_ERR_ARG, "tk_expand_quant: T=%d < 0", T);
+    if (k < 1) return fail(TK_ERR_ARG, "tk_expand_quant: k=%d < 1", k);
+    if (k > TK_MAX_TOPK)
+        return fail(TK_ERR_UNSUPPORTED, "tk_expand_quant: k=%d > %d", k, TK_MAX_TOPK);
+    if (rows_capacity < 0) return fail(TK_ERR_ARG, "tk_expand_quant: rows_capacity < 0");
+    if (mode != TK_EXPAND_BF16 && mode != TK_EXPAND_FP8_E4M3_1X128)
+        return fail(TK_ERR_ARG, "tk_expand_quant: unknown mode %d", mode);
+    if (H <= 0 || H % 8 != 0)
+        return fail(TK_ERR_ARG, "tk_expand_quant: H=%d must be a positive multiple of 8", H);
+    if (mode == TK_EXPAND_FP8_E4M3_1X128 && H % 128 != 0)
+        return fail(TK_ERR_ARG, "tk_expand_quant: FP8 1x128 mode needs H %% 128 == 0 (H=%d)", H);
+    if (mode == TK_EXPAND_FP8_E4M3_1X128 && scales == nullptr && rows_capacity > 0)
+        return fail(TK_ERR_ARG, "tk_expand_quant: FP8 mode needs scales");
+    if (T == 0 || rows_capacity == 0) return tk::ok();
+    if (x_bf16 == nullptr || pos == nullptr || out == nullptr)
+        return fail(TK_ERR_ARG, "tk_expand_quant: NULL tensor pointer");
+    if (!tk::aligned16(x_bf16) || !tk::aligned16(out) || !tk::aligned4(pos) ||
+        (scales && !tk::aligned4(scales)))
+        return fail(TK_ERR_ARG, "tk_expand_quant: x/out must be 16-byte aligned, pos/scales 4-byte");
+
+    const auto* x = static_cast<const uint16_t*>(x_bf16);
+    const dim3 grid((T + tk::kWavesPerBlock - 1) / tk::kWavesPerBlock), block(tk::kBlock);
+    hipError_t e;
+    if (mode == TK_EXPAND_FP8_E4M3_1X128) {
+        auto* q = static_cast<uint8_t*>(out);
+        switch (k) {
+        case 1: e = tk::launch(expand_fp8_kernel<1>, grid, block, 0, stream, x, T, H, k, pos, q, scales, rows_capacity); break;
+        case 2: e = tk::launch(expand_fp8_kernel<2>, grid, block, 0, stream, x, T, H, k, pos, q, scales, rows_capacity); break;
+        case 4: e = tk::launch(expand_fp8_kernel<4>, grid, block, 0, stream, x, T, H, k, pos, q, scales, rows_capacity); break;
+        case 6: e = tk::launch(expand_fp8_kernel<6>, grid, block, 0, stream, x, T, H, k, pos, q, scales, rows_capacity); break;
+        case 8: e = tk::launch(expand_fp8_kernel<8>, grid, block, 0, stream, x, T, H, k, pos, q, scales, rows_capacity); break;
+        default: e = tk::launch(expand_fp8_kernel<0>, grid, block, 0, stream, x, T, H, k, pos, q, scales, rows_capacity); break;
+        }
+    } else {
+        auto* o = static_cast<uint16_t*>(out);
+        switch (k) {
+        case 1: e = tk::launch(expand_bf16_kernel<1>, grid, block, 0, stream, x, T, H, k, pos, o, rows_capacity); break;
+        case 2: e = tk::launch(expand_bf16_kernel<2>, grid, block, 0, stream, x, T, H, k, pos, o, rows_capacity); break;
+        case 4: e = tk::launch(expand_bf16_kernel<4>, grid, block, 0, stream, x, T, H, k, pos, o, rows_capacity); break;
+        case 8: e = tk::launch(expand_bf16_kernel<8>, grid, block, 0, stream, x, T, H, k, pos, o, rows_capacity); break;
+        default: e = tk::launch(expand_bf16_kernel<0>, grid, block, 0, stream, x, T, H, k, pos, o, rows_capacity); break;
+        }
+    }
+    return tk::launched(e, "tk_expand_quant");
+}
+
+TK_EXPORT tk_status tk_expert_standin(const uint8_t* xq, const float* scales,
+                                      const int32_t* n_rows, int64_t rows_capacity, int32_t H,
+                                      float mult, void* y_bf16, hipStream_t stream)
+{
+    using tk::fail;
+    if (rows_capacity < 0) return fail(TK_ERR_ARG, "tk_expert_standin: rows_capacity < 0");
+    if (H <= 0 || H % 128 != 0)
+        return fail(TK_ERR_ARG, "tk_expert_standin: H=%d must be a positive multiple of 128", H);
+    if (rows_capacity == 0) return tk::ok();
+    if (xq == nullptr || scales == nullptr || n_rows == nullptr || y_bf16 == nullptr)
+        return fail(TK_ERR_ARG, "tk_expert_standin: NULL pointer");
+    if (!tk::aligned16(xq) || !tk::aligned16(y_bf16) || !tk::aligned4(scales) ||
+        !tk::aligned4(n_rows))
+        return fail(TK_ERR_ARG, "tk_expert_standin: xq/y must be 16-byte aligned");
+    const int chunks = (H + kChunkFp8 - 1) / kChunkFp8;
+    const hipError_t e = tk::launch(standin_kernel, dim3(grid_for(rows_capacity * chunks)),
+                                    dim3(tk::kBlock), 0, stream, xq, scales, n_rows, rows_capacity,
+                                    H, mult, static_cast<uint16_t*>(y_bf16), chunks);
+    return tk::launched(e, "tk_expert_standin");
+}

@@ -1,0 +1,118 @@
+// Internal helpers shared by the HIP sources of libtk (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <tuple>
+#include <utility>
+
+#include "tk.h"
+
+#define TK_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace tk {
+
+// ---------------------------------------------------------------- host side
+// Record a failure for tk_last_error() and return `status`.
+tk_status fail(tk_status status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+// Clear the error text and return TK_OK.
+tk_status ok();
+// Turn a HIP launch result into a status.
+tk_status launched(hipError_t e, const char* what);
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Launch kernel `k` with arguments converted to its exact parameter types;
+// returns the launch status directly (no sticky-error lookups).
+template <typename... KA, typename... PA>
+hipError_t launch(void (*k)(KA...), dim3 grid, dim3 block, size_t lds_bytes, hipStream_t s,
+                  PA&&... pa)
+{
+    std::tuple<KA...> args(std::forward<PA>(pa)...);
+    void* argv[sizeof...(KA) ? sizeof...(KA) : 1];
+    std::apply([&](auto&... a) {
+        int i = 0;
+        ((argv[i++] = static_cast<void*>(&a)), ...);
+    }, args);
+    return hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, argv, lds_bytes, s);
+}
+
+// Waves of 64 lanes; the kernels here use 256-lane workgroups (4 waves).
+constexpr int kWave = 64;
+constexpr int kBlock = 256;
+constexpr int kWavesPerBlock = kBlock / kWave;
+
+// ------------------------------------------------------------- device side
+// Wave-uniform copy of a value (the first active lane's), kept in an SGPR.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// bf16 pair packed in a 32-bit word -> two fp32 values (exact widening).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Cross-lane moves inside a row of 16 lanes (DPP), full exec assumed.
+// kQuadXor1 / kQuadXor2: quad_perm [1,0,3,2] / [2,3,0,1]; kHalfMirror: lane
+// i <-> 7-i within 8 lanes; kMirror: lane i <-> 15-i within 16 lanes.
+constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kHalfMirror = 0x141, kMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
+{
+    return static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Maximum over each aligned run of 8 lanes, returned to every lane of the run.
+__device__ __forceinline__ float max_run8(float v)
+{
+    v = fmaxf(v, dpp_f32<kQuadXor1>(v));
+    v = fmaxf(v, dpp_f32<kQuadXor2>(v));
+    return fmaxf(v, dpp_f32<kHalfMirror>(v));
+}
+
+// Maximum over each aligned run of `width` lanes (a power of two <= 64),
+// returned to every lane of the run.
+__device__ __forceinline__ uint32_t max_run_u32(uint32_t v, int width)
+{
+    if (width >= 2) v = max(v, dpp_u32<kQuadXor1>(v));
+    if (width >= 4) v = max(v, dpp_u32<kQuadXor2>(v));
+    if (width >= 8) v = max(v, dpp_u32<kHalfMirror>(v));
+    if (width >= 16) v = max(v, dpp_u32<kMirror>(v));
+    if (width >= 32) {
+        const uint32_t r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31);
+        const uint32_t r2 = __builtin_amdgcn_readlane(v, 47), r3 = __builtin_amdgcn_readlane(v, 63);
+        const uint32_t lo = max(r0, r1), hi = max(r2, r3);
+        v = (width == 64) ? max(lo, hi) : ((threadIdx.x & 32) ? hi : lo);
+    }
+    return v;
+}
+
+// Maximum over the whole wave as a wave-uniform (SGPR) value.
+__device__ __forceinline__ uint32_t max_wave_u32(uint32_t v)
+{
+    v = max(v, dpp_u32<kQuadXor1>(v));
+    v = max(v, dpp_u32<kQuadXor2>(v));
+    v = max(v, dpp_u32<kHalfMirror>(v));
+    v = max(v, dpp_u32<kMirror>(v));
+    const uint32_t r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31);
+    const uint32_t r2 = __builtin_amdgcn_readlane(v, 47), r3 = __builtin_amdgcn_readlane(v, 63);
+    return max(max(r0, r1), max(r2, r3));
+}
+
+// Two fp32 -> two bf16 (round to nearest even, hardware convert) packed.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    const __bf16 a = static_cast<__bf16>(lo);
+    const __bf16 b = static_cast<__bf16>(hi);
+    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
+           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+}
+
+}  // namespace tk

@@ -1,0 +1,196 @@
+"""GPU parity of tk_expand_quant, tk_expert_standin and tk_reduce against the
+CPU oracle.
+
+FP8 codes and scales, bf16 copies and stand-in outputs: bit-exact.  Combine:
+|gpu - ref| <= 1e-2 + 1e-2*|ref| per element (the fraction of bit-identical
+elements is reported and expected to be high).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from moe_routing_amd import synth
+from tk_testutil import combine_report, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+tk = pytest.importorskip("moe_routing_amd")
+
+
+def _routing(T, E, k, seed, lo=0, hi=None):
+    rng = np.random.default_rng(seed)
+    idx = synth.random_routing(rng, T, E, k)
+    counts, offsets, pos, row_src = oracle.map_routes(idx, E, lo, E if hi is None else hi)
+    return idx, pos, int(offsets[-1])
+
+
+def _special_rows(H):
+    """Rows that hit the codec's corners: zeros, signed zeros, clamped tiny
+    blocks, blocks with scale exactly 1 holding every bf16 magnitude <= 448,
+    E4M3 midpoints (ties) and their bf16 neighbours, huge values."""
+    rows = [np.zeros(H, np.float32), np.full(H, -0.0, np.float32)]
+    t = np.full(H, 3e-5, np.float32); t[1::2] *= -1; rows.append(t)
+    # every bf16 pattern with magnitude <= 448, packed 127 per block + one 448
+    allb = np.arange(0, 0x8000, dtype=np.uint32)
+    vals = (allb << 16).view(np.float32)
+    vals = vals[np.isfinite(vals) & (np.abs(vals) <= 448.0)]
+    vals = np.concatenate([vals, -vals])
+    n_blocks = int(np.ceil(vals.size / 127))
+    blocks = np.zeros((n_blocks, 128), np.float32)
+    blocks[:, 0] = 448.0
+    flat = blocks[:, 1:].reshape(-1)
+    flat[: vals.size] = vals
+    blocks[:, 1:] = flat.reshape(n_blocks, 127)
+    per_row = H // 128
+    n_rows = int(np.ceil(n_blocks / per_row))
+    pad = np.zeros((n_rows * per_row - n_blocks, 128), np.float32)
+    pad[:, 0] = 448.0
+    rows.extend(np.concatenate([blocks, pad]).reshape(n_rows, H))
+    # scales that are not powers of two: amax 300, 1.7, 1e-3 with ramps
+    for amax in (300.0, 1.7, 1e-3, 6.0e4):
+        r = np.linspace(-amax, amax, H).astype(np.float32)
+        rows.append(r)
+    return synth.bf16_bits(np.stack(rows))
+
+
+def _check_expand_fp8(x_bits, pos, R):
+    T, H = x_bits.shape
+    xq, sc = tk.tk_expand_quant(to_dev(x_bits, bf16=True), to_dev(pos), tk.TK_EXPAND_FP8_E4M3_1X128, R)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quant_row(x_bits)           # per token, once
+    g_q, g_s = to_host(xq), to_host(sc)
+    for j in range(pos.shape[1]):
+        valid = pos[:, j] >= 0
+        rows = pos[valid, j]
+        bad = np.nonzero((g_q[rows] != q_ref[valid]).any(1))[0]
+        assert bad.size == 0, f"slot {j}: FP8 bytes differ for {bad.size} tokens, first {np.nonzero(valid)[0][bad[:3]]}"
+        assert np.array_equal(g_s[rows], s_ref[valid]), f"slot {j}: scales differ"
+
+
+@pytest.mark.parametrize("T,E,k,H", [(64, 16, 2, 256), (100, 32, 3, 1152), (513, 64, 8, 7168),
+                                     (37, 8, 1, 128), (200, 16, 4, 3072)])
+def test_expand_fp8_random(T, E, k, H):
+    idx, pos, R = _routing(T, E, k, T + H)
+    rng = np.random.default_rng(H)
+    x = synth.normal_bf16(rng, (T, H))
+    x[::7] = synth.bf16_bits(synth.normal_f32(rng, (len(x[::7]), H)) * np.float32(50.0))
+    _check_expand_fp8(x, pos, R)
+
+
+@pytest.mark.parametrize("H", [1024, 7168])
+def test_expand_fp8_codec_corners(H):
+    x = _special_rows(H)
+    T = x.shape[0]
+    pos = np.arange(T, dtype=np.int32)[:, None]
+    _check_expand_fp8(x, pos, T)
+
+
+def test_expand_fp8_v3_full():
+    cfg = synth.v3_gate(0)
+    idx, _ = oracle.route(cfg["logits"], cfg["bias"], cfg["k"], **cfg["route"])
+    _, offsets, pos, _ = oracle.map_routes(idx, 256)
+    x = synth.v3_hidden(0)
+    _check_expand_fp8(x, pos, int(offsets[-1]))
+
+
+def test_expand_skips_and_capacity():
+    T, E, k, H = 300, 16, 4, 512
+    idx, pos, R = _routing(T, E, k, 11, lo=4, hi=12)     # masked routes have pos -1
+    cap = R - 5                                            # last rows beyond capacity
+    x = synth.normal_bf16(np.random.default_rng(12), (T, H))
+    sentinel = 0x5A
+    out = torch.full((cap + 3, H), sentinel, dtype=torch.uint8, device="cuda")
+    sc = torch.full((cap + 3, H // 128), -1.0, dtype=torch.float32, device="cuda")
+    tk.tk_expand_quant(to_dev(x, bf16=True), to_dev(pos), tk.TK_EXPAND_FP8_E4M3_1X128, cap,
+                       out=out, scales=sc)
+    ref_q, ref_s = oracle.expand(x, pos, 1, cap)
+    g = to_host(out)
+    assert np.array_equal(g[:cap], ref_q) and np.array_equal(to_host(sc)[:cap], ref_s)
+    assert np.all(g[cap:] == sentinel), "wrote beyond rows_capacity"
+
+
+@pytest.mark.parametrize("T,E,k,H", [(64, 16, 2, 256), (129, 8, 3, 520), (10, 4, 1, 8),
+                                     (300, 64, 8, 7168)])
+def test_expand_bf16(T, E, k, H):
+    idx, pos, R = _routing(T, E, k, T * 3 + H)
+    x = synth.normal_bf16(np.random.default_rng(T), (T, H))
+    out, _ = tk.tk_expand_quant(to_dev(x, bf16=True), to_dev(pos), tk.TK_EXPAND_BF16, R)
+    ref, _ = oracle.expand(x, pos, 0, R)
+    assert np.array_equal(to_host(out), ref)
+
+
+def test_expand_zero_tokens():
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    pos = torch.empty((0, 2), dtype=torch.int32, device="cuda")
+    tk.tk_expand_quant(x, pos, tk.TK_EXPAND_FP8_E4M3_1X128, 0)
+    torch.cuda.synchronize()
+
+
+def test_standin_matches_oracle():
+    T, E, k, H = 400, 16, 3, 1024
+    idx, pos, R = _routing(T, E, k, 21)
+    x = synth.normal_bf16(np.random.default_rng(22), (T, H))
+    xq, sc = tk.tk_expand_quant(to_dev(x, bf16=True), to_dev(pos), tk.TK_EXPAND_FP8_E4M3_1X128, R + 7)
+    n_rows = torch.tensor([R], dtype=torch.int32, device="cuda")
+    y = tk.tk_expert_standin(xq, sc, n_rows, 0.5)
+    torch.cuda.synchronize()
+    q, s = oracle.expand(x, pos, 1, R)
+    ref = oracle.standin(q, s, 0.5)
+    assert np.array_equal(to_host(y)[:R], ref)
+
+
+# ------------------------------------------------------------------ reduce --
+def _check_reduce(y_bits, pos, w, sample=None):
+    out = tk.tk_reduce(to_dev(y_bits, bf16=True), to_dev(pos), to_dev(w))
+    torch.cuda.synchronize()
+    g = to_host(out)
+    if sample is None:
+        ref = oracle.reduce(y_bits, pos, w)
+    else:
+        ref = oracle.reduce(y_bits, pos[sample], w[sample])
+        g = g[sample]
+    rep = combine_report(g, ref)
+    assert rep["ok"], rep
+    assert rep["bit_exact_frac"] > 0.98, rep
+    return rep
+
+
+@pytest.mark.parametrize("T,E,k,H", [(64, 16, 2, 256), (333, 32, 8, 1032), (50, 8, 1, 128),
+                                     (77, 64, 6, 7168), (40, 64, 12, 512)])
+def test_reduce_random(T, E, k, H):
+    idx, pos, R = _routing(T, E, k, T + k)
+    rng = np.random.default_rng(H + k)
+    y = synth.normal_bf16(rng, (R, H))
+    w = rng.random((T, k)).astype(np.float32)
+    _check_reduce(y, pos, w)
+
+
+def test_reduce_masked_and_empty_tokens():
+    T, E, k, H = 400, 64, 8, 1024
+    idx, pos, R = _routing(T, E, k, 31, lo=32, hi=40)
+    rng = np.random.default_rng(32)
+    y = synth.normal_bf16(rng, (max(R, 1), H))
+    w = rng.random((T, k)).astype(np.float32)
+    assert (pos < 0).all(1).any(), "want tokens without local routes"
+    rep = _check_reduce(y, pos, w)
+    out = to_host(tk.tk_reduce(to_dev(y, bf16=True), to_dev(pos), to_dev(w)))
+    assert np.all(out[(pos < 0).all(1)] == 0)
+
+
+def test_reduce_exact_gather():
+    T, H = 256, 2048
+    y = synth.normal_bf16(np.random.default_rng(33), (T, H))
+    perm = np.random.default_rng(34).permutation(T).astype(np.int32)[:, None]
+    out = tk.tk_reduce(to_dev(y, bf16=True), to_dev(perm), to_dev(np.ones((T, 1), np.float32)))
+    assert np.array_equal(to_host(out), y[perm[:, 0]])
+
+
+def test_reduce_v3_full_sampled():
+    cfg = synth.v3_gate(0)
+    idx, w = oracle.route(cfg["logits"], cfg["bias"], cfg["k"], **cfg["route"])
+    _, offsets, pos, _ = oracle.map_routes(idx, 256)
+    y = synth.v3_expert_out(0)
+    sample = np.random.default_rng(35).choice(8192, 256, replace=False)
+    sample = np.concatenate([sample, [0, 8191]])
+    _check_reduce(y, pos, w.astype(np.float32), sample)

@@ -1,0 +1,170 @@
+"""GPU parity of tk_route and tk_map against the CPU oracle.
+
+Indices, counts, offsets, positions and row_src: bit-exact.  Weights: within
+the fp32-vs-fp64 tolerance of tk_testutil (W_RTOL).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from moe_routing_amd import synth
+from tk_testutil import W_ATOL, W_RTOL, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+tk = pytest.importorskip("moe_routing_amd")
+
+
+def _route_both(logits, bias, k, **r):
+    opts = tk.RouteOpts(**r)
+    idx, w = tk.tk_route(to_dev(logits), None if bias is None else to_dev(bias), k, opts)
+    torch.cuda.synchronize()
+    o_idx, o_w = oracle.route(logits, bias, k, **r)
+    return to_host(idx), to_host(w), o_idx, o_w
+
+
+def _assert_route(logits, bias, k, **r):
+    g_idx, g_w, o_idx, o_w = _route_both(logits, bias, k, **r)
+    bad = np.nonzero((g_idx != o_idx).any(1))[0]
+    assert bad.size == 0, f"{bad.size} tokens differ, first t={bad[:5]}: {g_idx[bad[:2]]} vs {o_idx[bad[:2]]}"
+    assert np.allclose(g_w, o_w, rtol=W_RTOL, atol=W_ATOL), np.abs(g_w - o_w).max()
+    return g_idx, g_w
+
+
+def test_route_tiny_softmax():
+    cfg = synth.tiny(0)
+    _assert_route(cfg["logits"], None, cfg["k"], **cfg["route"])
+
+
+def test_route_v3_gate_full():
+    cfg = synth.v3_gate(0)
+    idx, w = _assert_route(cfg["logits"], cfg["bias"], cfg["k"], **cfg["route"])
+    assert np.allclose(w.astype(np.float64).sum(1), 2.5, rtol=8 * 2.0 ** -24)
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 8, 1), (3, 16, 4), (257, 64, 6), (130, 100, 7),
+                                   (129, 128, 8), (200, 256, 8), (65, 512, 16),
+                                   (33, 1024, 32), (50, 5, 5)])
+@pytest.mark.parametrize("score", ["softmax", "sigmoid", "sigmoid_bias", "softmax_raw", "sigmoid_raw"])
+def test_route_plain_shapes(T, E, k, score):
+    rng = np.random.default_rng(T * 1000 + E + k)
+    logits = synth.normal_f32(rng, (T, E))
+    bias = rng.uniform(-0.1, 0.1, E).astype(np.float32) if score == "sigmoid_bias" else None
+    r = dict(score=tk.TK_SCORE_SOFTMAX if score.startswith("softmax") else tk.TK_SCORE_SIGMOID,
+             n_groups=1, topk_groups=1, group_topn=0,
+             renormalize=0 if score.endswith("raw") else 1, route_scale=1.5)
+    _assert_route(logits, bias, k, **r)
+
+
+@pytest.mark.parametrize("E,n_groups,topk_groups,group_topn,k", [
+    (256, 8, 4, 2, 8), (64, 8, 3, 1, 5), (16, 4, 2, 2, 3), (128, 4, 2, 3, 6),
+    (512, 8, 2, 2, 8), (1024, 16, 4, 2, 8), (256, 2, 1, 2, 4), (256, 4, 4, 2, 8),
+])
+def test_route_group_limited(E, n_groups, topk_groups, group_topn, k):
+    rng = np.random.default_rng(E + n_groups * 10 + k)
+    T = 333
+    logits = synth.normal_f32(rng, (T, E))
+    bias = rng.uniform(-0.1, 0.1, E).astype(np.float32)
+    r = dict(score=tk.TK_SCORE_SIGMOID, n_groups=n_groups, topk_groups=topk_groups,
+             group_topn=group_topn, renormalize=1, route_scale=2.5)
+    _assert_route(logits, bias, k, **r)
+    _assert_route(logits, None, k, **r)
+
+
+def test_route_ties_and_signed_zero():
+    rng = np.random.default_rng(5)
+    for E, k in ((16, 4), (256, 8), (64, 64)):
+        x = rng.integers(-3, 4, (300, E)).astype(np.float32)
+        x[rng.random(x.shape) < 0.2] = -0.0
+        _assert_route(x, None, k, score=0, n_groups=1, topk_groups=1, group_topn=0,
+                      renormalize=1, route_scale=1.0)
+        _assert_route(x, None, min(k, 8), score=1, n_groups=1, topk_groups=1, group_topn=0,
+                      renormalize=1, route_scale=1.0)
+    x = rng.integers(-2, 3, (300, 256)).astype(np.float32)
+    _assert_route(x, None, 8, score=1, n_groups=8, topk_groups=4, group_topn=2,
+                  renormalize=1, route_scale=2.5)
+
+
+def test_route_extreme_logits():
+    rng = np.random.default_rng(6)
+    x = synth.normal_f32(rng, (200, 256)) * np.float32(40.0)   # sigmoid saturates to 0/1
+    x[:, :3] = np.float32([-100.0, 100.0, 88.5])
+    _assert_route(x, None, 8, score=1, n_groups=8, topk_groups=4, group_topn=2,
+                  renormalize=1, route_scale=2.5)
+
+
+def test_route_zero_tokens():
+    opts = tk.RouteOpts(score=1)
+    idx, w = tk.tk_route(torch.empty((0, 64), device="cuda"), None, 4, opts)
+    torch.cuda.synchronize()
+    assert idx.shape == (0, 4)
+
+
+# --------------------------------------------------------------------- map --
+def _map_both(idx, E, lo, hi):
+    g = tk.tk_map(to_dev(idx), E, lo, hi)
+    torch.cuda.synchronize()
+    counts, offsets, pos, row_src = (to_host(t) for t in g)
+    o = oracle.map_routes(idx, E, lo, hi)
+    return (counts, offsets, pos, row_src), o
+
+
+def _assert_map(idx, E, lo, hi):
+    (c, o, p, rs), (oc, oo, op, ors) = _map_both(idx, E, lo, hi)
+    assert np.array_equal(c, oc), "counts"
+    assert np.array_equal(o, oo), "offsets"
+    bad = np.nonzero((p != op).any(1))[0]
+    assert bad.size == 0, f"pos differs at tokens {bad[:5]}"
+    R = int(oo[-1])
+    assert np.array_equal(rs[:R], ors), "row_src"
+    return c, o, p
+
+
+def test_map_v3_gate_full():
+    cfg = synth.v3_gate(0)
+    r = cfg["route"]
+    idx, _ = oracle.route(cfg["logits"], cfg["bias"], cfg["k"], **r)
+    c, o, p = _assert_map(idx, 256, 0, 256)
+    assert o[-1] == 8192 * 8
+
+
+@pytest.mark.parametrize("T,E,k,lo,hi", [
+    (1, 8, 1, 0, 8), (31, 16, 2, 0, 16), (1000, 256, 8, 32, 64), (4097, 256, 8, 0, 256),
+    (777, 64, 3, 0, 64), (300, 1024, 32, 0, 1024), (512, 1024, 9, 100, 900),
+    (2049, 32, 4, 7, 8), (5000, 160, 6, 0, 160), (70000, 256, 8, 0, 256),
+])
+def test_map_random_routing(T, E, k, lo, hi):
+    rng = np.random.default_rng(T + E)
+    idx = synth.random_routing(rng, T, E, k)
+    _assert_map(idx, E, lo, hi)
+
+
+def test_map_repeats_and_out_of_range_ids():
+    rng = np.random.default_rng(7)
+    T, E, k = 600, 32, 6
+    idx = rng.integers(-3, E + 3, (T, k)).astype(np.int32)   # repeats and invalid ids
+    _assert_map(idx, E, 0, E)
+    _assert_map(idx, E, 10, 20)
+
+
+def test_map_empty_experts_and_all_masked():
+    rng = np.random.default_rng(8)
+    idx = synth.random_routing(rng, 500, 16, 4) + 16          # all ids in [16, 32)
+    (c, o, p, _), _ = _map_both(idx.astype(np.int32), 64, 0, 16)
+    assert np.all(c == 0) and np.all(o == 0) and np.all(p == -1)
+
+
+def test_map_zero_tokens():
+    counts, offsets, pos, _ = tk.tk_map(torch.empty((0, 8), dtype=torch.int32, device="cuda"), 256)
+    torch.cuda.synchronize()
+    assert np.all(to_host(counts) == 0) and np.all(to_host(offsets) == 0)
+
+
+def test_map_deterministic():
+    rng = np.random.default_rng(9)
+    idx = to_dev(synth.random_routing(rng, 8192, 256, 8))
+    a = [to_host(t) for t in tk.tk_map(idx, 256)]
+    b = [to_host(t) for t in tk.tk_map(idx, 256)]
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
