@@ -1,0 +1,171 @@
+"""CPU tests of the C-ABI boundary: the library loads, exports every entry
+point include/tk.h declares, and its host-side argument checks reject bad
+calls before anything is launched (no GPU is touched by these calls).  Also
+checks that the product package never reaches the oracle.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tk.h")
+LIB = os.path.join(ROOT, "moe_routing_amd", "libtk.so")
+
+ARG, UNSUP = -1, -2
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:tk_status|size_t|const char\*)\s+(tk_\w+)\s*\(",
+                                 text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        import __graft_entry__
+        __graft_entry__.build()
+    L = ctypes.CDLL(LIB)
+    L.tk_last_error.restype = ctypes.c_char_p
+    for name in ("tk_route", "tk_map", "tk_expand_quant", "tk_reduce", "tk_expert_standin"):
+        getattr(L, name).restype = ctypes.c_int32
+    L.tk_map_workspace_bytes.restype = ctypes.c_size_t
+    return L
+
+
+def test_header_declares_the_entry_points():
+    assert _declared() == sorted(["tk_last_error", "tk_route", "tk_map_workspace_bytes", "tk_map",
+                                  "tk_expand_quant", "tk_reduce", "tk_expert_standin"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+    # nothing but tk_* is exported (hidden visibility for the rest)
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert exported == set(_declared())
+
+
+class RouteOpts(ctypes.Structure):
+    _fields_ = [("score", ctypes.c_int32), ("n_groups", ctypes.c_int32),
+                ("topk_groups", ctypes.c_int32), ("group_topn", ctypes.c_int32),
+                ("renormalize", ctypes.c_int32), ("route_scale", ctypes.c_float)]
+
+
+FAKE = ctypes.c_void_p(0x10000)        # aligned fake device address, never dereferenced
+MIS = ctypes.c_void_p(0x10004)         # 4-aligned, not 16-aligned
+MIS1 = ctypes.c_void_p(0x10001)
+
+
+def _route(lib, T, E, k, opts, logits=FAKE, bias=None, idx=FAKE, w=FAKE):
+    L = ctypes.c_int32
+    return lib.tk_route(logits, bias, L(T), L(E), L(k), ctypes.byref(opts) if opts else None,
+                        idx, w, None)
+
+
+def test_route_rejects_bad_arguments(lib):
+    o = RouteOpts(1, 8, 4, 2, 1, 2.5)
+    assert _route(lib, 4, 256, 8, None) == ARG and b"opts" in lib.tk_last_error()
+    assert _route(lib, -1, 256, 8, o) == ARG
+    assert _route(lib, 4, 256, 0, o) == ARG
+    assert _route(lib, 4, 16, 17, RouteOpts(0, 1, 1, 0, 1, 1.0)) == ARG          # k > E
+    assert _route(lib, 4, 2048, 8, RouteOpts(0, 1, 1, 0, 1, 1.0)) == UNSUP       # E > max
+    assert _route(lib, 4, 256, 33, RouteOpts(0, 1, 1, 0, 1, 1.0)) == UNSUP       # k > max
+    assert _route(lib, 4, 250, 8, RouteOpts(1, 8, 4, 2, 1, 2.5)) == ARG          # E % groups
+    assert _route(lib, 4, 256, 8, RouteOpts(1, 8, 9, 2, 1, 2.5)) == ARG          # topk_groups
+    assert _route(lib, 4, 256, 8, RouteOpts(1, 8, 4, 0, 1, 2.5)) == ARG          # group_topn
+    assert _route(lib, 4, 256, 40, RouteOpts(1, 8, 1, 2, 1, 2.5)) in (ARG, UNSUP)
+    assert _route(lib, 4, 256, 9, RouteOpts(1, 64, 2, 2, 1, 2.5)) == ARG         # 2*4 < 9
+    assert b"fewer than k" in lib.tk_last_error()
+    assert _route(lib, 4, 96, 4, RouteOpts(1, 8, 4, 2, 1, 2.5)) == UNSUP         # 12/2 lanes
+    assert _route(lib, 4, 256, 8, RouteOpts(7, 1, 1, 0, 1, 1.0)) == ARG          # score
+    assert _route(lib, 4, 256, 8, RouteOpts(0, 1, 1, 0, 1, 1.0), bias=FAKE) == ARG
+    assert _route(lib, 4, 256, 8, o, logits=None) == ARG
+    assert _route(lib, 4, 256, 8, o, logits=MIS) == ARG                          # 16B for E%4==0
+    assert _route(lib, 4, 256, 8, o, idx=MIS1) == ARG
+    assert _route(lib, 0, 256, 8, o, logits=None, idx=None, w=None) == 0         # T == 0 no-op
+    assert lib.tk_last_error() == b""
+
+
+def _map(lib, T, k, E, lo, hi, ws_bytes=1 << 20, counts=FAKE, ws=FAKE, idx=FAKE, pos=FAKE):
+    I = ctypes.c_int32
+    return lib.tk_map(idx, I(T), I(k), I(E), I(lo), I(hi), counts, FAKE, pos, None, ws,
+                      ctypes.c_size_t(ws_bytes), None)
+
+
+def test_map_rejects_bad_arguments(lib):
+    assert _map(lib, -1, 8, 256, 0, 256) == ARG
+    assert _map(lib, 4, 0, 256, 0, 256) == ARG
+    assert _map(lib, 4, 33, 256, 0, 256) == UNSUP
+    assert _map(lib, 4, 8, 4096, 0, 256) == UNSUP
+    assert _map(lib, 4, 8, 256, 32, 32) == ARG
+    assert _map(lib, 4, 8, 256, -1, 32) == ARG
+    assert _map(lib, 4, 8, 256, 0, 257) == ARG
+    assert _map(lib, 8192, 8, 256, 0, 256, ws_bytes=100) == ARG
+    assert b"workspace" in lib.tk_last_error()
+    assert _map(lib, 4, 8, 256, 0, 256, counts=None) == ARG
+    assert _map(lib, 4, 8, 256, 0, 256, ws=MIS1) == ARG
+    assert _map(lib, 4, 8, 256, 0, 256, idx=None) == ARG
+
+
+def test_map_workspace_bytes(lib):
+    f = lib.tk_map_workspace_bytes
+    assert f(0, 8, 256) == 0
+    assert f(8192, 8, 256) == 16 * 256 * 4          # 512-token tiles
+    assert f(32768, 8, 32) == 32 * 32 * 4           # 1024-token tiles
+    assert f(1, 1, 1024) == 1024 * 4
+
+
+def _expand(lib, T, H, k, mode, cap, x=FAKE, out=FAKE, scales=FAKE, pos=FAKE):
+    I = ctypes.c_int32
+    return lib.tk_expand_quant(x, I(T), I(H), I(k), pos, I(mode), out, scales,
+                               ctypes.c_int64(cap), None)
+
+
+def test_expand_rejects_bad_arguments(lib):
+    assert _expand(lib, -1, 256, 2, 0, 8) == ARG
+    assert _expand(lib, 4, 200, 2, 1, 8) == ARG                       # H % 128 in FP8
+    assert b"128" in lib.tk_last_error()
+    assert _expand(lib, 4, 260, 2, 0, 8) == ARG                       # H % 8
+    assert _expand(lib, 4, 256, 2, 5, 8) == ARG                       # mode
+    assert _expand(lib, 4, 256, 2, 1, 8, scales=None) == ARG
+    assert _expand(lib, 4, 256, 2, 1, -1) == ARG
+    assert _expand(lib, 4, 256, 2, 1, 8, out=MIS) == ARG
+    assert _expand(lib, 4, 256, 2, 1, 8, x=None) == ARG
+    assert _expand(lib, 4, 256, 40, 1, 8) == UNSUP
+    assert _expand(lib, 0, 256, 2, 1, 8, x=None, out=None, pos=None) == 0
+
+
+def test_reduce_and_standin_reject_bad_arguments(lib):
+    I = ctypes.c_int32
+    r = lambda T, k, H, rows=8, y=FAKE, out=FAKE: lib.tk_reduce(
+        y, ctypes.c_int64(rows), FAKE, FAKE, I(T), I(k), I(H), out, None)
+    assert r(-1, 2, 256) == ARG
+    assert r(4, 0, 256) == ARG
+    assert r(4, 33, 256) == UNSUP
+    assert r(4, 2, 12) == ARG
+    assert r(4, 2, 256, rows=-1) == ARG
+    assert r(4, 2, 256, out=MIS) == ARG
+    assert r(4, 2, 256, y=None) == ARG
+    assert r(0, 2, 256, y=None, out=None) == 0
+    s = lambda cap, H, xq=FAKE: lib.tk_expert_standin(xq, FAKE, FAKE, ctypes.c_int64(cap), I(H),
+                                                      ctypes.c_float(0.5), FAKE, None)
+    assert s(8, 100) == ARG
+    assert s(-1, 128) == ARG
+    assert s(8, 128, xq=None) == ARG
+    assert s(8, 128, xq=MIS) == ARG
+    assert s(0, 128) == 0
+
+
+def test_product_path_never_uses_the_oracle():
+    pkg = os.path.join(ROOT, "moe_routing_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert not re.search(r"import\s+oracle|from\s+oracle|liboracle|\borc_\w+",
+                                     text), f
