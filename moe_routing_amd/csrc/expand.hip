@@ -15,9 +15,10 @@
 //
 // Quotient x/scale: Markstein's correction on the reciprocal,
 //   inv = RN(1/scale); q0 = RN(x*inv); r = fma(-q0, scale, x); q = fma(r, inv, q0)
-// (P. Markstein, IBM J. Res. Dev. 34(1), 1990), which equals the IEEE
-// quotient RN(x/scale) for every (x, scale) this kernel can see; the exhaustive
-// host test of the bf16 x / block-scale domain is tests/test_quotient_domain.py.
+// (P. Markstein, IBM J. Res. Dev. 34(1), 1990), with the sign of x restored
+// for x = -0.  It equals the IEEE quotient RN(x/scale) for every (x, scale)
+// this kernel can see, except where both lie below 2^-10 and so encode to the
+// same signed zero; tests/test_quotient_domain.py enumerates that domain.
 // FP8 encoding: gfx950's v_cvt_pk_fp8_f32 (OCP E4M3FN, round to nearest even).
 #include "tk_internal.h"
 
@@ -26,13 +27,19 @@ namespace {
 constexpr int kChunkFp8 = 1024;   // columns per unit, FP8 mode (16 per lane)
 constexpr int kChunkBf16 = 512;   // columns per unit, bf16 mode (8 per lane)
 
+// x / scale for scale > 0.  The correction step maps x = -0 to +0 (the sum
+// +0 + -0 rounds to +0), so the sign of x is put back; for x != 0 the sign
+// is already right and copysign changes nothing.
 __device__ __forceinline__ float quotient(float x, float scale, float inv)
 {
     const float q0 = x * inv;
     const float r = __builtin_fmaf(-q0, scale, x);
-    return __builtin_fmaf(r, inv, q0);
+    return __builtin_copysignf(__builtin_fmaf(r, inv, q0), x);
 }
 
+// Four quotients -> four E4M3 codes (gfx950 hardware convert: OCP E4M3FN,
+// round to nearest even).  amax / RN(amax/448) can exceed 448 by one fp32
+// ulp; such values round to 448 like every value below 464.
 __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d)
 {
     int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);

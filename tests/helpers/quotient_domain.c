@@ -4,8 +4,9 @@
  *     inv = RN(1/scale); q0 = RN(x*inv); r = fma(-q0, scale, x); q = fma(r, inv, q0)
  * (Markstein's correction step).  The domain is every pair the kernel can
  * see: amax = a bf16 magnitude >= 1e-4 or the clamp value 1e-4f,
- * scale = RN(amax/448), and x = every non-negative bf16 value <= amax (the
- * negative half follows by symmetry of round-to-nearest).  For each pair the
+ * scale = RN(amax/448), and x = every bf16 value with |x| <= amax, both
+ * signs (-0 included: the correction step alone would turn it into +0, so
+ * the kernel restores the sign of x).  For each pair the
  * shortcut must equal the IEEE quotient RN(x/scale) bit for bit, except where
  * both lie below 2^-10 -- half the smallest E4M3 subnormal, so both encode to
  * the same signed zero.  (Differences occur only for x tiny against a huge
@@ -31,12 +32,12 @@ static long long check_amax(float amax, long long* pairs, long long* tiny)
     const float inv = 1.0f / scale;
     const float kTiny = 0x1p-10f;
     long long bad = 0, n = 0;
-    for (uint32_t h = 0; h < 0x7F80u; ++h) {
+    for (uint32_t h = 0; h < 0x10000u; ++h) {
         const float x = f32(h << 16);
-        if (x > amax) break;
+        if (!(fabsf(x) <= amax)) continue;
         const float q0 = x * inv;
         const float r = fmaf(-q0, scale, x);
-        const float q = fmaf(r, inv, q0);
+        const float q = copysignf(fmaf(r, inv, q0), x);
         const float ref = x / scale;
         if (bits(q) != bits(ref)) {
             if (fabsf(q) < kTiny && fabsf(ref) < kTiny && signbit(q) == signbit(ref)) {

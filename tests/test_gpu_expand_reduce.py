@@ -54,6 +54,13 @@ def _special_rows(H):
     return synth.bf16_bits(np.stack(rows))
 
 
+def _describe(x_bits, g_row, o_row, scale):
+    d = np.nonzero(g_row != o_row)[0][:4]
+    xs = oracle.bf16_to_f32(x_bits[d])
+    return [(int(c), float(xs[i]), float(scale[c // 128]), hex(g_row[c]), hex(o_row[c]))
+            for i, c in enumerate(d)]
+
+
 def _check_expand_fp8(x_bits, pos, R):
     T, H = x_bits.shape
     xq, sc = tk.tk_expand_quant(to_dev(x_bits, bf16=True), to_dev(pos), tk.TK_EXPAND_FP8_E4M3_1X128, R)
@@ -64,7 +71,11 @@ def _check_expand_fp8(x_bits, pos, R):
         valid = pos[:, j] >= 0
         rows = pos[valid, j]
         bad = np.nonzero((g_q[rows] != q_ref[valid]).any(1))[0]
-        assert bad.size == 0, f"slot {j}: FP8 bytes differ for {bad.size} tokens, first {np.nonzero(valid)[0][bad[:3]]}"
+        if bad.size:
+            t = int(np.nonzero(valid)[0][bad[0]])
+            detail = _describe(x_bits[t], g_q[pos[t, j]], q_ref[t], s_ref[t])
+            raise AssertionError(f"slot {j}: FP8 bytes differ for {bad.size} tokens, first t={t}: "
+                                 f"(col, x, scale, gpu, oracle) {detail}")
         assert np.array_equal(g_s[rows], s_ref[valid]), f"slot {j}: scales differ"
 
 
@@ -84,6 +95,26 @@ def test_expand_fp8_codec_corners(H):
     T = x.shape[0]
     pos = np.arange(T, dtype=np.int32)[:, None]
     _check_expand_fp8(x, pos, T)
+
+
+def test_expand_fp8_quotient_just_above_448():
+    """Every bf16 block maximum m >= 1e-4 whose quotient m / RN(m/448) rounds
+    above 448 in fp32 (about 9 % of them): the code must still be 448."""
+    h = np.arange(0x3800, 0x7F80, dtype=np.uint32)
+    a = (h << 16).view(np.float32)
+    a = a[a >= np.float32(1e-4)]
+    over = a[(a / (a / np.float32(448.0)).astype(np.float32)).astype(np.float32) > 448.0]
+    assert over.size > 1000
+    H = 1024
+    rng = np.random.default_rng(50)
+    blocks = rng.uniform(-1, 1, (over.size, 128)).astype(np.float32) * over[:, None]
+    blocks[:, 0] = over
+    blocks[1::2, 0] *= -1                                  # negative maxima too
+    n_rows = int(np.ceil(over.size / (H // 128)))
+    pad = np.ones((n_rows * (H // 128) - over.size, 128), np.float32)
+    x = synth.bf16_bits(np.concatenate([blocks, pad]).reshape(n_rows, H))
+    pos = np.arange(n_rows, dtype=np.int32)[:, None]
+    _check_expand_fp8(x, pos, n_rows)
 
 
 def test_expand_fp8_v3_full():
