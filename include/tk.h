@@ -154,7 +154,7 @@ size_t tk_map_workspace_bytes(int32_t T, int32_t k, int32_t n_local);
  * offsets   device, int32 (n_local + 1) out
  * pos       device, int32 (T, k) out
  * row_src   device, int32 (T * k) out, or NULL; entries r >= R are untouched
- * workspace device, >= tk_map_workspace_bytes(T, k, n_local) bytes, 4-byte
+ * workspace device, >= tk_map_workspace_bytes(T, k, n_local) bytes, 16-byte
  *           aligned; scratch, contents on entry ignored
  */
 tk_status tk_map(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,

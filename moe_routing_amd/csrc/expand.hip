@@ -5,14 +5,19 @@
 // shape, "剛剛，DeepSeek開始頻繁更新：Tile Kernels、DeepEP V2", section 性能表現).
 // Also tk_expert_standin, the dequantise-and-scale harness kernel.
 //
-// Token-major: one wave per token, walking the row in 1024-column chunks.
-// Each lane reads 16 bf16 (two 16-byte loads), so every 8-lane group holds one
-// 128-column quantisation block; the block amax is a 3-step DPP butterfly
-// inside the group.  The token's k row indices are loaded once.  The token
-// is read once and its 16 code bytes per lane are stored to each of its k
-// rows (one 1 KiB contiguous segment per row per wave), so HBM traffic is
-// T*H*2 read + R*H written, not R*H*2 read.
-//
+// Token-major: one workgroup of 8 waves per token.  Wave w walks the row's
+// 1024-column chunks w, w+8, ...; each lane reads 16 bf16 (two 16-byte
+// loads), so every 8-lane group holds one 128-column quantisation block and
+// the block amax is a 3-step DPP butterfly inside the group.  The token is
+// read once, quantised once, and its 16 code bytes per lane are stored to
+// each of its k rows (one 1 KiB contiguous segment per row per wave), so HBM
+// traffic is T*H*2 read + R*H written, not R*H*2 read.  The expanded rows are
+// written once and not read again by this pipeline, so they go out through
+// nontemporal stores; the token is read with ordinary loads (on MI355X the
+// nontemporal hint on these reads measured slower).  All scale writes of a
+// row come from one workgroup, so no 4-byte scale shares a cache line with
+// another workgroup's.
+
 // Quotient x/scale: Markstein's correction on the reciprocal,
 //   inv = RN(1/scale); q0 = RN(x*inv); r = fma(-q0, scale, x); q = fma(r, inv, q0)
 // (P. Markstein, IBM J. Res. Dev. 34(1), 1990), with the sign of x restored
@@ -24,8 +29,9 @@
 
 namespace {
 
-constexpr int kChunkFp8 = 1024;   // columns per unit, FP8 mode (16 per lane)
-constexpr int kChunkBf16 = 512;   // columns per unit, bf16 mode (8 per lane)
+constexpr int kChunkFp8 = 1024;   // columns per wave step, FP8 mode (16 per lane)
+constexpr int kChunkBf16 = 512;   // columns per wave step, bf16 mode (8 per lane)
+constexpr int kExpandWaves = 8;   // waves per workgroup (one token per workgroup)
 
 // x / scale for scale > 0.  The correction step maps x = -0 to +0 (the sum
 // +0 + -0 rounds to +0), so the sign of x is put back; for x != 0 the sign
@@ -60,29 +66,29 @@ __device__ __forceinline__ void token_rows(const int32_t* __restrict__ pos, int 
     for (int j = 0; j < KMAX; ++j) rows[j] = (r[j] >= 0 && r[j] < cap) ? r[j] : -1;
 }
 
-// One token per wave; K > 0 is a compile-time k, K == 0 a runtime k.
+// One token per workgroup; K > 0 is a compile-time k, K == 0 a runtime k.
 template <int K>
-__global__ __launch_bounds__(tk::kBlock) void expand_fp8_kernel(
+__global__ __launch_bounds__(tk::kWave * kExpandWaves) void expand_fp8_kernel(
     const uint16_t* __restrict__ x, int T, int H, int k_rt, const int32_t* __restrict__ pos,
     uint8_t* __restrict__ out, float* __restrict__ scales, int64_t cap)
 {
     constexpr int KMAX = K > 0 ? K : TK_MAX_TOPK;
     const int k = K > 0 ? K : k_rt;
     const int lane = threadIdx.x & (tk::kWave - 1);
-    const int t = blockIdx.x * tk::kWavesPerBlock + tk::uniform(threadIdx.x / tk::kWave);
+    const int wave = tk::uniform(threadIdx.x / tk::kWave);
+    const int t = blockIdx.x;
     if (t >= T) return;
     const int nb = H / 128;
     int64_t rows[KMAX];
     token_rows<KMAX>(pos, t, k, cap, rows);
     const uint16_t* xt = x + static_cast<size_t>(t) * H;
-    for (int col0 = 0; col0 < H; col0 += kChunkFp8) {
-        const int col = col0 + lane * 16;
+    for (int col = wave * kChunkFp8 + lane * 16; col - lane * 16 < H; col += kExpandWaves * kChunkFp8) {
+        // H % 128 == 0: an 8-lane group (128 columns) is wholly inside or outside the row
         const bool active = col < H;
-        uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
+        tk::u32x4 a = tk::u32x4{0u, 0u, 0u, 0u}, b = a;
         if (active) {
-            const uint4* src = reinterpret_cast<const uint4*>(xt + col);
-            a = src[0];
-            b = src[1];
+            a = tk::load16(xt + col);
+            b = tk::load16(xt + col + 8);
         }
         const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
         float v[16];
@@ -97,7 +103,7 @@ __global__ __launch_bounds__(tk::kBlock) void expand_fp8_kernel(
         amax = fmaxf(tk::max_run8(amax), 1e-4f);   // one 128-column block per 8 lanes
         const float scale = amax / 448.0f;
         const float inv = 1.0f / scale;
-        uint4 q;
+        tk::u32x4 q;
         q.x = pack_fp8x4(quotient(v[0], scale, inv), quotient(v[1], scale, inv),
                          quotient(v[2], scale, inv), quotient(v[3], scale, inv));
         q.y = pack_fp8x4(quotient(v[4], scale, inv), quotient(v[5], scale, inv),
@@ -110,7 +116,7 @@ __global__ __launch_bounds__(tk::kBlock) void expand_fp8_kernel(
 #pragma unroll
             for (int j = 0; j < KMAX; ++j) {
                 if (rows[j] < 0) continue;
-                *reinterpret_cast<uint4*>(out + static_cast<size_t>(rows[j]) * H + col) = q;
+                tk::store_stream(out + static_cast<size_t>(rows[j]) * H + col, q);
                 if ((lane & 7) == 0) scales[static_cast<size_t>(rows[j]) * nb + col / 128] = scale;
             }
         }
@@ -118,23 +124,24 @@ __global__ __launch_bounds__(tk::kBlock) void expand_fp8_kernel(
 }
 
 template <int K>
-__global__ __launch_bounds__(tk::kBlock) void expand_bf16_kernel(
+__global__ __launch_bounds__(tk::kWave * kExpandWaves) void expand_bf16_kernel(
     const uint16_t* __restrict__ x, int T, int H, int k_rt, const int32_t* __restrict__ pos,
     uint16_t* __restrict__ out, int64_t cap)
 {
     constexpr int KMAX = K > 0 ? K : TK_MAX_TOPK;
     const int k = K > 0 ? K : k_rt;
     const int lane = threadIdx.x & (tk::kWave - 1);
-    const int t = blockIdx.x * tk::kWavesPerBlock + tk::uniform(threadIdx.x / tk::kWave);
+    const int wave = tk::uniform(threadIdx.x / tk::kWave);
+    const int t = blockIdx.x;
     if (t >= T) return;
     int64_t rows[KMAX];
     token_rows<KMAX>(pos, t, k, cap, rows);
     const uint16_t* xt = x + static_cast<size_t>(t) * H;
-    for (int col = lane * 8; col < H; col += kChunkBf16) {
-        const uint4 a = *reinterpret_cast<const uint4*>(xt + col);
+    for (int col = wave * kChunkBf16 + lane * 8; col < H; col += kExpandWaves * kChunkBf16) {
+        const tk::u32x4 a = tk::load16(xt + col);
 #pragma unroll
         for (int j = 0; j < KMAX; ++j)
-            if (rows[j] >= 0) *reinterpret_cast<uint4*>(out + static_cast<size_t>(rows[j]) * H + col) = a;
+            if (rows[j] >= 0) tk::store_stream(out + static_cast<size_t>(rows[j]) * H + col, a);
     }
 }
 
@@ -211,7 +218,7 @@ TK_EXPORT tk_status tk_expand_quant(const void* x_bf16, int32_t T, int32_t H, in
         return fail(TK_ERR_ARG, "tk_expand_quant: x/out must be 16-byte aligned, pos/scales 4-byte");
 
     const auto* x = static_cast<const uint16_t*>(x_bf16);
-    const dim3 grid((T + tk::kWavesPerBlock - 1) / tk::kWavesPerBlock), block(tk::kBlock);
+    const dim3 grid(static_cast<unsigned>(T)), block(tk::kWave * kExpandWaves);
     hipError_t e;
     if (mode == TK_EXPAND_FP8_E4M3_1X128) {
         auto* q = static_cast<uint8_t*>(out);

@@ -3,31 +3,53 @@
 // ops of TileKernels' moe/ module ("刚刚！DeepSeek开源高性能GPU算子库TileKernels",
 // item moe/).
 //
-// Three launches, no atomics on global memory, so every output is a pure
+// Tokens are cut into tiles of 32*S tokens (S sub-tiles of 32).  Two launches
+// at the usual sizes, no atomics on global memory, so every output is a pure
 // function of topk_idx:
-//   1. hist    one workgroup per tile of tokens: LDS histogram of the local
-//              experts -> tile_counts[tile][e] in the workspace
-//   2. scan    one workgroup: per expert, exclusive scan over tiles; block
-//              scan over experts -> counts, offsets; the workspace becomes
-//              tile_base[tile][e] = first row of expert e owned by the tile
-//   3. scatter one workgroup per tile: a bit mask per (expert, 32-token
-//              sub-tile) in LDS; the rank of token t among the tile's tokens
-//              routed to e is (tokens of e in earlier sub-tiles) + popcount of
-//              the bits below t in its own sub-tile.  pos = tile_base + rank.
+//   1. count  one workgroup per tile: LDS histogram of the tile's local
+//             routes -> cnt[e][tile] (expert-major) in the workspace
+//   2. place  one workgroup per tile: per expert, the sum over all tiles
+//             (total) and over the tiles before this one (before); a block
+//             scan of the totals gives offsets; then a bit mask per
+//             (expert, sub-tile) in LDS ranks the tile's tokens:
+//               pos = offsets[e] + before[e] + (tokens of e in earlier
+//                     sub-tiles) + popcount(bits below t in t's sub-tile)
+// When there are many tiles, a third launch (scan, between the two) turns the
+// counts into per-tile prefixes once, so that place reads one column instead
+// of a whole row per expert.
 // Ranks follow token order, which is the stable order because a token is
 // routed to an expert at most once (repeats in a row are dropped).
 #include "tk_internal.h"
 
 namespace {
 
-constexpr int kSub = 32;                 // tokens per sub-tile (one mask word)
-constexpr int kMaskWords = 4096;         // LDS budget: n_local * sub-tiles <= this
+constexpr int kSub = 32;               // tokens per sub-tile (one mask word)
+constexpr int kThreads = 256;          // threads of the count and place kernels
+constexpr int kTargetTiles = 32;       // tiles aimed for, for parallelism
+constexpr int kMaxFusedTiles = 64;     // beyond this, prefixes come from the scan kernel
+constexpr int kLdsWords = 12288;       // place kernel LDS budget (48 KiB)
+constexpr int kScanThreads = 1024;
 
-// Sub-tiles per tile for n_local local experts (tile = 32 * S tokens).
-__host__ __device__ inline int subtiles_per_tile(int n_local)
+struct Tiling {
+    int S;          // sub-tiles per tile
+    int tile;       // tokens per tile
+    int n_tiles;
+    int pitch;      // ints per expert row of cnt (n_tiles rounded up to 4)
+    bool fused;     // place computes prefixes itself
+};
+
+__host__ inline Tiling tiling(int T, int n_local)
 {
-    int s = kMaskWords / n_local;
-    return s > 32 ? 32 : (s < 1 ? 1 : s);
+    Tiling g{};
+    int s_max = (kLdsWords - n_local) / (2 * n_local);  // mask + before words per tile
+    s_max = s_max < 1 ? 1 : (s_max > 64 ? 64 : s_max);
+    int s = (T + kSub * kTargetTiles - 1) / (kSub * kTargetTiles);
+    g.S = s < 1 ? 1 : (s > s_max ? s_max : s);
+    g.tile = g.S * kSub;
+    g.n_tiles = T > 0 ? (T + g.tile - 1) / g.tile : 0;
+    g.pitch = (g.n_tiles + 3) & ~3;
+    g.fused = g.n_tiles <= kMaxFusedTiles;
+    return g;
 }
 
 // Token t's k expert ids as local indices (id - lo); -1 for an id outside
@@ -50,92 +72,142 @@ __device__ __forceinline__ void load_local_ids(const int32_t* __restrict__ idx, 
 }
 
 template <int KMAX>
-__global__ __launch_bounds__(tk::kBlock) void map_hist_kernel(
-    const int32_t* __restrict__ idx, int T, int k, int lo, int hi, int tile_tokens,
-    int32_t* __restrict__ tile_counts)
+__global__ __launch_bounds__(kThreads) void map_count_kernel(
+    const int32_t* __restrict__ idx, int T, int k, int lo, int hi, int tile_tokens, int pitch,
+    int32_t* __restrict__ cnt)
 {
-    extern __shared__ int32_t cnt[];
+    extern __shared__ int32_t hist[];
     const int nl = hi - lo;
-    for (int i = threadIdx.x; i < nl; i += tk::kBlock) cnt[i] = 0;
+    for (int i = threadIdx.x; i < nl; i += kThreads) hist[i] = 0;
     __syncthreads();
     const int t0 = blockIdx.x * tile_tokens;
-    for (int tl = threadIdx.x; tl < tile_tokens; tl += tk::kBlock) {
+    for (int tl = threadIdx.x; tl < tile_tokens; tl += kThreads) {
         const int t = t0 + tl;
         if (t >= T) break;
         int e[KMAX];
         load_local_ids<KMAX>(idx, t, k, lo, hi, e);
 #pragma unroll
         for (int j = 0; j < KMAX; ++j)
-            if (e[j] >= 0) atomicAdd(&cnt[e[j]], 1);
+            if (e[j] >= 0) atomicAdd(&hist[e[j]], 1);
     }
     __syncthreads();
-    int32_t* out = tile_counts + static_cast<size_t>(blockIdx.x) * nl;
-    for (int i = threadIdx.x; i < nl; i += tk::kBlock) out[i] = cnt[i];
+    for (int i = threadIdx.x; i < nl; i += kThreads)
+        cnt[static_cast<size_t>(i) * pitch + blockIdx.x] = hist[i];
+    // the padding columns [n_tiles, pitch) of every row are read as part of
+    // whole int4s later: the first tile writes them as zeros
+    if (blockIdx.x == 0) {
+        for (int i = threadIdx.x; i < nl; i += kThreads)
+            for (int c = gridDim.x; c < pitch; ++c) cnt[static_cast<size_t>(i) * pitch + c] = 0;
+    }
 }
 
-constexpr int kScanThreads = 1024;
-
-// tile_counts[tile][e] -> tile_base[tile][e] (in place); counts, offsets.
+// Many tiles: cnt[e][tile] -> exclusive prefix over tiles (in place), and
+// totals[e] = the sum over all tiles.  One workgroup, a thread per expert.
 __global__ __launch_bounds__(kScanThreads) void map_scan_kernel(
-    int32_t* __restrict__ tiles, int n_tiles, int nl, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets)
+    int32_t* __restrict__ cnt, int n_tiles, int pitch, int nl, int32_t* __restrict__ totals)
 {
-    __shared__ int32_t tot[TK_MAX_EXPERTS];
-    __shared__ int32_t wave_sum[kScanThreads / tk::kWave];
-    // per expert: exclusive scan over tiles (coalesced across experts)
     for (int e = threadIdx.x; e < nl; e += kScanThreads) {
+        int32_t* row = cnt + static_cast<size_t>(e) * pitch;
         int32_t run = 0;
-        for (int tile = 0; tile < n_tiles; ++tile) {
-            int32_t* p = tiles + static_cast<size_t>(tile) * nl + e;
-            const int32_t c = *p;
-            *p = run;
-            run += c;
+        for (int i = 0; i < n_tiles; i += 4) {   // pitch % 4 == 0: whole int4s
+            int4 c = *reinterpret_cast<const int4*>(row + i);
+            const int4 ex = make_int4(run, run + c.x, run + c.x + c.y, run + c.x + c.y + c.z);
+            run += c.x + c.y + c.z + c.w;
+            *reinterpret_cast<int4*>(row + i) = ex;
         }
-        tot[e] = run;
-        counts[e] = run;
+        totals[e] = run;
     }
-    __syncthreads();
-    // exclusive scan of tot over experts (nl <= 1024 = one element per thread)
+}
+
+// Exclusive scan over the workgroup of per-thread values (kThreads threads);
+// returns this thread's exclusive prefix and writes the grand total to *total.
+__device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* wave_sums, int32_t* total)
+{
     const int lane = threadIdx.x & (tk::kWave - 1), wave = threadIdx.x / tk::kWave;
-    const int v = (threadIdx.x < nl) ? tot[threadIdx.x] : 0;
-    int inc = v;
+    int32_t inc = v;
 #pragma unroll
     for (int off = 1; off < tk::kWave; off <<= 1) {
-        const int o = __shfl_up(inc, off);
+        const int32_t o = __shfl_up(inc, off);
         if (lane >= off) inc += o;
     }
-    if (lane == tk::kWave - 1) wave_sum[wave] = inc;
+    if (lane == tk::kWave - 1) wave_sums[wave] = inc;
     __syncthreads();
-    int before = 0;
-    for (int w = 0; w < wave; ++w) before += wave_sum[w];
-    const int excl = before + inc - v;
-    __syncthreads();
-    if (threadIdx.x < nl) {
-        tot[threadIdx.x] = excl;
-        offsets[threadIdx.x] = excl;
+    int32_t before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / tk::kWave; ++w) {
+        const int32_t s = wave_sums[w];
+        before += (w < wave) ? s : 0;
+        all += s;
     }
-    if (threadIdx.x == nl - 1) offsets[nl] = excl + v;
-    __syncthreads();
-    for (int e = threadIdx.x; e < nl; e += kScanThreads) {
-        const int32_t base = tot[e];
-        for (int tile = 0; tile < n_tiles; ++tile) tiles[static_cast<size_t>(tile) * nl + e] += base;
-    }
+    *total = all;
+    return before + inc - v;
 }
 
 template <int KMAX>
-__global__ __launch_bounds__(tk::kBlock) void map_scatter_kernel(
-    const int32_t* __restrict__ idx, int T, int k, int lo, int hi, int S,
-    const int32_t* __restrict__ tile_base, int32_t* __restrict__ pos, int32_t* __restrict__ row_src)
+__global__ __launch_bounds__(kThreads) void map_place_kernel(
+    const int32_t* __restrict__ idx, int T, int k, int lo, int hi, int S, int n_tiles, int pitch,
+    int fused, const int32_t* __restrict__ cnt, const int32_t* __restrict__ totals,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ pos,
+    int32_t* __restrict__ row_src)
 {
     extern __shared__ uint32_t lds[];
+    __shared__ int32_t wave_sums[kThreads / tk::kWave];
     const int nl = hi - lo;
-    uint32_t* mask = lds;              // [nl][S]
-    uint32_t* before = lds + nl * S;   // [nl][S] tokens of e in earlier sub-tiles
+    uint32_t* mask = lds;                                          // [nl][S]
+    uint32_t* before_sub = lds + nl * S;                           // [nl][S]
+    int32_t* base = reinterpret_cast<int32_t*>(lds + 2 * nl * S);  // [nl]
+    const int tile = blockIdx.x;
     const int tile_tokens = S * kSub;
-    for (int i = threadIdx.x; i < nl * S; i += tk::kBlock) mask[i] = 0;
+
+    // 1. per expert: total over all tiles, sum over the tiles before this one
+    //    (this thread owns the ept consecutive experts [e0, e0 + ept))
+    const int ept = (nl + kThreads - 1) / kThreads;
+    const int e0 = threadIdx.x * ept;
+    int32_t my_total = 0;
+    for (int i = 0; i < ept; ++i) {
+        const int e = e0 + i;
+        if (e >= nl) break;
+        const int32_t* row = cnt + static_cast<size_t>(e) * pitch;
+        int32_t tot = 0, bef = 0;
+        if (fused) {
+            for (int c = 0; c < n_tiles; c += 4) {
+                const int4 v = *reinterpret_cast<const int4*>(row + c);
+                tot += v.x + v.y + v.z + v.w;
+                bef += (c < tile ? v.x : 0) + (c + 1 < tile ? v.y : 0) +
+                       (c + 2 < tile ? v.z : 0) + (c + 3 < tile ? v.w : 0);
+            }
+        } else {
+            tot = totals[e];
+            bef = row[tile];
+        }
+        base[e] = bef;
+        my_total += tot;
+        // keep the expert's total until the scan below has produced offsets
+        before_sub[e] = static_cast<uint32_t>(tot);
+    }
     __syncthreads();
-    const int t0 = blockIdx.x * tile_tokens;
-    for (int tl = threadIdx.x; tl < tile_tokens; tl += tk::kBlock) {
+    // 2. offsets: exclusive scan of the totals over experts
+    int32_t grand = 0;
+    int32_t run = block_exclusive_scan(my_total, wave_sums, &grand);
+    for (int i = 0; i < ept; ++i) {
+        const int e = e0 + i;
+        if (e >= nl) break;
+        const int32_t tot = static_cast<int32_t>(before_sub[e]);
+        if (tile == 0) {
+            counts[e] = tot;
+            offsets[e] = run;
+        }
+        base[e] += run;
+        run += tot;
+    }
+    if (tile == 0 && threadIdx.x == 0) offsets[nl] = grand;
+    __syncthreads();
+
+    // 3. rank the tile's tokens per expert: bit masks per (expert, sub-tile)
+    for (int i = threadIdx.x; i < nl * S; i += kThreads) mask[i] = 0;
+    __syncthreads();
+    const int t0 = tile * tile_tokens;
+    for (int tl = threadIdx.x; tl < tile_tokens; tl += kThreads) {
         const int t = t0 + tl;
         if (t >= T) break;
         int e[KMAX];
@@ -145,16 +217,15 @@ __global__ __launch_bounds__(tk::kBlock) void map_scatter_kernel(
             if (e[j] >= 0) atomicOr(&mask[e[j] * S + tl / kSub], 1u << (tl % kSub));
     }
     __syncthreads();
-    for (int ex = threadIdx.x; ex < nl; ex += tk::kBlock) {
-        uint32_t run = 0;
+    for (int ex = threadIdx.x; ex < nl; ex += kThreads) {
+        uint32_t r = 0;
         for (int s = 0; s < S; ++s) {
-            before[ex * S + s] = run;
-            run += __popc(mask[ex * S + s]);
+            before_sub[ex * S + s] = r;
+            r += __popc(mask[ex * S + s]);
         }
     }
     __syncthreads();
-    const int32_t* base = tile_base + static_cast<size_t>(blockIdx.x) * nl;
-    for (int tl = threadIdx.x; tl < tile_tokens; tl += tk::kBlock) {
+    for (int tl = threadIdx.x; tl < tile_tokens; tl += kThreads) {
         const int t = t0 + tl;
         if (t >= T) break;
         int e[KMAX];
@@ -167,11 +238,20 @@ __global__ __launch_bounds__(tk::kBlock) void map_scatter_kernel(
             int32_t p = -1;
             if (e[j] >= 0) {
                 const int w = e[j] * S + s;
-                p = base[e[j]] + static_cast<int32_t>(before[w] + __popc(mask[w] & below));
+                p = base[e[j]] + static_cast<int32_t>(before_sub[w] + __popc(mask[w] & below));
                 if (row_src != nullptr) row_src[p] = t;
             }
             pos[static_cast<size_t>(t) * k + j] = p;
         }
+    }
+}
+
+// Zero counts and offsets when no token is given.
+__global__ void map_empty_kernel(int nl, int32_t* __restrict__ counts, int32_t* __restrict__ offsets)
+{
+    for (int i = threadIdx.x; i <= nl; i += blockDim.x) {
+        if (i < nl) counts[i] = 0;
+        offsets[i] = 0;
     }
 }
 
@@ -181,9 +261,9 @@ TK_EXPORT size_t tk_map_workspace_bytes(int32_t T, int32_t k, int32_t n_local)
 {
     (void)k;
     if (T <= 0 || n_local <= 0) return 0;
-    const int tile_tokens = subtiles_per_tile(n_local) * kSub;
-    const size_t n_tiles = (static_cast<size_t>(T) + tile_tokens - 1) / tile_tokens;
-    return n_tiles * static_cast<size_t>(n_local) * sizeof(int32_t);
+    const Tiling g = tiling(T, n_local);
+    // cnt[n_local][pitch] + totals[n_local]
+    return (static_cast<size_t>(n_local) * g.pitch + static_cast<size_t>(n_local)) * sizeof(int32_t);
 }
 
 TK_EXPORT tk_status tk_map(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
@@ -211,33 +291,40 @@ TK_EXPORT tk_status tk_map(const int32_t* topk_idx, int32_t T, int32_t k, int32_
     const size_t need = tk_map_workspace_bytes(T, k, nl);
     if (workspace_bytes < need)
         return fail(TK_ERR_ARG, "tk_map: workspace of %zu bytes < %zu needed", workspace_bytes, need);
-    if (need > 0 && (workspace == nullptr || !tk::aligned4(workspace)))
-        return fail(TK_ERR_ARG, "tk_map: workspace NULL or not 4-byte aligned");
+    if (need > 0 && (workspace == nullptr || !tk::aligned16(workspace)))
+        return fail(TK_ERR_ARG, "tk_map: workspace NULL or not 16-byte aligned");
+    if (!tk::aligned4(counts) || !tk::aligned4(offsets) || (pos && !tk::aligned4(pos)) ||
+        (row_src && !tk::aligned4(row_src)) || (topk_idx && !tk::aligned4(topk_idx)))
+        return fail(TK_ERR_ARG, "tk_map: int32 tensors must be 4-byte aligned");
 
-    const int S = subtiles_per_tile(nl);
-    const int tile_tokens = S * kSub;
-    const int n_tiles = (T + tile_tokens - 1) / tile_tokens;
-    int32_t* tiles = static_cast<int32_t*>(workspace);
-    const dim3 block(tk::kBlock);
-    hipError_t e = hipSuccess;
-    if (n_tiles > 0) {
-        e = (k <= 8)
-            ? tk::launch(map_hist_kernel<8>, dim3(n_tiles), block, nl * sizeof(int32_t), stream,
-                         topk_idx, T, k, local_begin, local_end, tile_tokens, tiles)
-            : tk::launch(map_hist_kernel<TK_MAX_TOPK>, dim3(n_tiles), block, nl * sizeof(int32_t),
-                         stream, topk_idx, T, k, local_begin, local_end, tile_tokens, tiles);
-        if (e != hipSuccess) return tk::launched(e, "tk_map (hist)");
+    hipError_t e;
+    if (T == 0) {
+        e = tk::launch(map_empty_kernel, dim3(1), dim3(kThreads), 0, stream, nl, counts, offsets);
+        return tk::launched(e, "tk_map (empty)");
     }
-    e = tk::launch(map_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, tiles, n_tiles, nl,
-                   counts, offsets);
-    if (e != hipSuccess) return tk::launched(e, "tk_map (scan)");
-    if (n_tiles > 0) {
-        const size_t lds = 2 * static_cast<size_t>(nl) * S * sizeof(uint32_t);
-        e = (k <= 8)
-            ? tk::launch(map_scatter_kernel<8>, dim3(n_tiles), block, lds, stream, topk_idx, T, k,
-                         local_begin, local_end, S, tiles, pos, row_src)
-            : tk::launch(map_scatter_kernel<TK_MAX_TOPK>, dim3(n_tiles), block, lds, stream,
-                         topk_idx, T, k, local_begin, local_end, S, tiles, pos, row_src);
+    const Tiling g = tiling(T, nl);
+    int32_t* cnt = static_cast<int32_t*>(workspace);
+    int32_t* totals = cnt + static_cast<size_t>(nl) * g.pitch;
+    const dim3 grid(g.n_tiles), block(kThreads);
+    const bool small_k = k <= 8;
+    e = small_k
+        ? tk::launch(map_count_kernel<8>, grid, block, nl * sizeof(int32_t), stream, topk_idx, T, k,
+                     local_begin, local_end, g.tile, g.pitch, cnt)
+        : tk::launch(map_count_kernel<TK_MAX_TOPK>, grid, block, nl * sizeof(int32_t), stream,
+                     topk_idx, T, k, local_begin, local_end, g.tile, g.pitch, cnt);
+    if (e != hipSuccess) return tk::launched(e, "tk_map (count)");
+    if (!g.fused) {
+        e = tk::launch(map_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, cnt, g.n_tiles,
+                       g.pitch, nl, totals);
+        if (e != hipSuccess) return tk::launched(e, "tk_map (scan)");
     }
-    return tk::launched(e, "tk_map (scatter)");
+    const size_t lds = (2 * static_cast<size_t>(nl) * g.S + nl) * sizeof(uint32_t);
+    e = small_k
+        ? tk::launch(map_place_kernel<8>, grid, block, lds, stream, topk_idx, T, k, local_begin,
+                     local_end, g.S, g.n_tiles, g.pitch, g.fused ? 1 : 0, cnt, totals, counts,
+                     offsets, pos, row_src)
+        : tk::launch(map_place_kernel<TK_MAX_TOPK>, grid, block, lds, stream, topk_idx, T, k,
+                     local_begin, local_end, g.S, g.n_tiles, g.pitch, g.fused ? 1 : 0, cnt, totals,
+                     counts, offsets, pos, row_src);
+    return tk::launched(e, "tk_map (place)");
 }

@@ -227,6 +227,188 @@ __global__ __launch_bounds__(tk::kBlock) void route_kernel(RouteArgs a)
     }
 }
 
+// ------------------------------------------------------------ fast kernel
+// The same selection, specialised at compile time for EPL <= 4 experts per
+// lane, a fixed k and one score function, with renormalised weights and
+// group_topn <= 2.  Differences in how it gets there (not in what it
+// computes):
+//  - each lane sorts its EPL keys once, descending, as 64-bit composites
+//    (key << 32 | EPL-1-i), so equal keys keep the lower expert first; a
+//    round of the top-k is then one wave max over the lanes' heads, a ballot
+//    whose lowest lane holds the lowest expert with that key, and a pop of
+//    the winning lane's list;
+//  - a group's top-2 keys come from a butterfly over its lanes that merges
+//    (largest, second largest) pairs;
+//  - the weights re-read the k chosen logits (cache hits) instead of
+//    carrying scores through the rounds.
+struct FastArgs {
+    const float* logits;
+    const float* bias;
+    int32_t* topk_idx;
+    float* topk_w;
+    int T, E;
+    int n_groups, topk_groups, group_topn, lanes_per_group;
+    float route_scale;
+};
+
+// (largest, second largest) of the union of two such pairs
+__device__ __forceinline__ void merge_top2(uint32_t& a1, uint32_t& a2, uint32_t b1, uint32_t b2)
+{
+    const uint32_t lo = min(a1, b1);
+    a1 = max(a1, b1);
+    a2 = max(lo, max(a2, b2));
+}
+
+template <int CTRL>
+__device__ __forceinline__ void merge_top2_dpp(uint32_t& m1, uint32_t& m2)
+{
+    merge_top2(m1, m2, tk::dpp_u32<CTRL>(m1), tk::dpp_u32<CTRL>(m2));
+}
+
+__device__ __forceinline__ void merge_top2_xor(uint32_t& m1, uint32_t& m2, int off)
+{
+    merge_top2(m1, m2, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m1), off)),
+               static_cast<uint32_t>(__shfl_xor(static_cast<int>(m2), off)));
+}
+
+__device__ __forceinline__ void cas_desc(uint64_t& a, uint64_t& b)
+{
+    const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
+    a = hi;
+    b = lo;
+}
+
+template <int EPL, int K, bool SIGMOID>
+__global__ __launch_bounds__(tk::kBlock) void route_fast_kernel(FastArgs a)
+{
+    static_assert(EPL == 1 || EPL == 2 || EPL == 4, "fast route handles 1, 2 or 4 experts per lane");
+    const int lane = threadIdx.x & (tk::kWave - 1);
+    const int t = blockIdx.x * tk::kWavesPerBlock + tk::uniform(threadIdx.x / tk::kWave);
+    if (t >= a.T) return;
+    const float* row = a.logits + static_cast<size_t>(t) * a.E;
+    const int e0 = lane * EPL;
+    const bool has_bias = a.bias != nullptr;
+
+    float x[EPL], b[EPL];
+    if (EPL == 4 && (a.E & 3) == 0) {
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f), w = v;
+        if (e0 < a.E) {
+            v = *reinterpret_cast<const float4*>(row + e0);
+            if (has_bias) w = *reinterpret_cast<const float4*>(a.bias + e0);
+        }
+        x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+        b[0] = w.x; b[1] = w.y; b[2] = w.z; b[3] = w.w;
+    } else {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const bool in = e0 + i < a.E;
+            x[i] = in ? row[e0 + i] : 0.f;
+            b[i] = (in && has_bias) ? a.bias[e0 + i] : 0.f;
+        }
+    }
+
+    // selection keys (order-preserving uint32, 0 = not eligible)
+    uint32_t key[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        float kf;
+        if constexpr (SIGMOID) {
+            const float sv = pinned_sigmoid(x[i]);
+            kf = has_bias ? sv + b[i] : sv;
+        } else {
+            kf = x[i];
+        }
+        key[i] = (e0 + i < a.E) ? order_key(kf) : 0u;
+    }
+
+    // group limit
+    if (a.n_groups > 1) {
+        uint32_t m1 = 0, m2 = 0;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            m2 = max(m2, min(m1, key[i]));
+            m1 = max(m1, key[i]);
+        }
+        const int lpg = a.lanes_per_group;
+        if (lpg >= 2) merge_top2_dpp<tk::kQuadXor1>(m1, m2);
+        if (lpg >= 4) merge_top2_dpp<tk::kQuadXor2>(m1, m2);
+        if (lpg >= 8) merge_top2_dpp<tk::kHalfMirror>(m1, m2);
+        if (lpg >= 16) merge_top2_dpp<tk::kMirror>(m1, m2);
+        if (lpg >= 32) merge_top2_xor(m1, m2, 16);
+        if (lpg >= 64) merge_top2_xor(m1, m2, 32);
+        const float gs = (a.group_topn == 2) ? key_value(m1) + key_value(m2) : key_value(m1);
+        const uint32_t og = order_key(gs);
+        const int g = lane / lpg;
+        int rank = 0;
+        for (int gp = 0; gp < a.n_groups; ++gp) {
+            const uint32_t o = static_cast<uint32_t>(readlane_i(static_cast<int>(og), gp * lpg));
+            rank += (o > og || (o == og && gp < g)) ? 1 : 0;
+        }
+        if (rank >= a.topk_groups) {
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) key[i] = 0;
+        }
+    }
+
+    // per-lane list, sorted descending; ties keep the lower expert first
+    uint64_t c[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) c[i] = (static_cast<uint64_t>(key[i]) << 32) | (EPL - 1 - i);
+    if constexpr (EPL == 2) {
+        cas_desc(c[0], c[1]);
+    } else if constexpr (EPL == 4) {
+        cas_desc(c[0], c[1]); cas_desc(c[2], c[3]);
+        cas_desc(c[0], c[2]); cas_desc(c[1], c[3]);
+        cas_desc(c[1], c[2]);
+    }
+
+    int my_e = 0;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        const uint32_t head = static_cast<uint32_t>(c[0] >> 32);
+        const uint32_t m = tk::max_wave_u32(head);
+        const uint64_t won = __ballot(head == m);
+        const int wl = tk::uniform(__ffsll(static_cast<long long>(won)) - 1);
+        const int li = EPL - 1 - readlane_i(static_cast<int>(static_cast<uint32_t>(c[0])), wl);
+        const int e = wl * EPL + li;
+        if (lane == j) my_e = e;
+        if (lane == wl) {
+#pragma unroll
+            for (int i = 0; i + 1 < EPL; ++i) c[i] = c[i + 1];
+            c[EPL - 1] = 0;
+        }
+    }
+
+    // weights over the chosen experts, sums in slot order
+    float sv = 0.f;
+    if (lane < K) {
+        const float xv = row[min(max(my_e, 0), a.E - 1)];
+        sv = xv;
+        if constexpr (SIGMOID) sv = pinned_sigmoid(xv);
+    }
+    float z = 0.f, v0 = 0.f;
+    if constexpr (SIGMOID) {
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            const float v = readlane_f(sv, j);
+            z = (j == 0) ? v : z + v;
+        }
+    } else {
+        v0 = readlane_f(sv, 0);
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            const float ev = expf(readlane_f(sv, j) - v0);
+            z = (j == 0) ? ev : z + ev;
+        }
+    }
+    if (lane < K) {
+        const float num = SIGMOID ? sv : expf(sv - v0);
+        const size_t o = static_cast<size_t>(t) * K + lane;
+        a.topk_idx[o] = my_e;
+        a.topk_w[o] = (num / z) * a.route_scale;
+    }
+}
+
 // Experts per lane: the power of two that fits E into one wave.
 int experts_per_lane(int E)
 {
@@ -282,6 +464,47 @@ TK_EXPORT tk_status tk_route(const float* logits, const float* bias, int32_t T, 
         return fail(TK_ERR_ARG, "tk_route: fp32/int32 tensors must be 4-byte aligned");
     if (epl >= 4 && E % 4 == 0 && !tk::aligned16(logits))
         return fail(TK_ERR_ARG, "tk_route: logits must be 16-byte aligned when E %% 4 == 0");
+
+    if (opts->renormalize && epl <= 4 && (opts->n_groups == 1 || opts->group_topn <= 2)) {
+        const FastArgs f{logits, bias, topk_idx, topk_w, T, E, opts->n_groups,
+                         opts->topk_groups, opts->group_topn, lpg, opts->route_scale};
+        const dim3 grid((T + tk::kWavesPerBlock - 1) / tk::kWavesPerBlock), block(tk::kBlock);
+        const bool sig = opts->score == TK_SCORE_SIGMOID;
+        hipError_t e = hipErrorInvalidValue;
+        bool launched = true;
+#define TK_ROUTE_FAST(EPL_, K_)                                                                    \
+    e = sig ? tk::launch(route_fast_kernel<EPL_, K_, true>, grid, block, 0, stream, f)             \
+            : tk::launch(route_fast_kernel<EPL_, K_, false>, grid, block, 0, stream, f)
+        switch (epl * 100 + k) {
+        case 101: TK_ROUTE_FAST(1, 1); break;
+        case 102: TK_ROUTE_FAST(1, 2); break;
+        case 103: TK_ROUTE_FAST(1, 3); break;
+        case 104: TK_ROUTE_FAST(1, 4); break;
+        case 105: TK_ROUTE_FAST(1, 5); break;
+        case 106: TK_ROUTE_FAST(1, 6); break;
+        case 107: TK_ROUTE_FAST(1, 7); break;
+        case 108: TK_ROUTE_FAST(1, 8); break;
+        case 201: TK_ROUTE_FAST(2, 1); break;
+        case 202: TK_ROUTE_FAST(2, 2); break;
+        case 203: TK_ROUTE_FAST(2, 3); break;
+        case 204: TK_ROUTE_FAST(2, 4); break;
+        case 205: TK_ROUTE_FAST(2, 5); break;
+        case 206: TK_ROUTE_FAST(2, 6); break;
+        case 207: TK_ROUTE_FAST(2, 7); break;
+        case 208: TK_ROUTE_FAST(2, 8); break;
+        case 401: TK_ROUTE_FAST(4, 1); break;
+        case 402: TK_ROUTE_FAST(4, 2); break;
+        case 403: TK_ROUTE_FAST(4, 3); break;
+        case 404: TK_ROUTE_FAST(4, 4); break;
+        case 405: TK_ROUTE_FAST(4, 5); break;
+        case 406: TK_ROUTE_FAST(4, 6); break;
+        case 407: TK_ROUTE_FAST(4, 7); break;
+        case 408: TK_ROUTE_FAST(4, 8); break;
+        default: launched = false; break;
+        }
+#undef TK_ROUTE_FAST
+        if (launched) return tk::launched(e, "tk_route");
+    }
 
     RouteArgs a{logits, bias, topk_idx, topk_w, T, E, k,
                 opts->score, opts->n_groups, opts->topk_groups, opts->group_topn,

@@ -48,6 +48,21 @@ constexpr int kWavesPerBlock = kBlock / kWave;
 // Wave-uniform copy of a value (the first active lane's), kept in an SGPR.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// 16 bytes as a native vector (the form the nontemporal builtins take).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte global load / store with the nontemporal (streaming) hint, for data
+// touched exactly once; compiles to global_load/store_dwordx4 ... nt.
+__device__ __forceinline__ u32x4 load_stream(const void* p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void store_stream(void* p, u32x4 v)
+{
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
 // bf16 pair packed in a 32-bit word -> two fp32 values (exact widening).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

@@ -109,15 +109,18 @@ def test_map_rejects_bad_arguments(lib):
     assert b"workspace" in lib.tk_last_error()
     assert _map(lib, 4, 8, 256, 0, 256, counts=None) == ARG
     assert _map(lib, 4, 8, 256, 0, 256, ws=MIS1) == ARG
+    assert _map(lib, 4, 8, 256, 0, 256, ws=MIS) == ARG     # workspace needs 16-byte alignment
     assert _map(lib, 4, 8, 256, 0, 256, idx=None) == ARG
 
 
 def test_map_workspace_bytes(lib):
+    # per-tile counts, one row of `pitch` ints per local expert (pitch = tiles
+    # rounded up to 4), plus one int per local expert
     f = lib.tk_map_workspace_bytes
     assert f(0, 8, 256) == 0
-    assert f(8192, 8, 256) == 16 * 256 * 4          # 512-token tiles
-    assert f(32768, 8, 32) == 32 * 32 * 4           # 1024-token tiles
-    assert f(1, 1, 1024) == 1024 * 4
+    assert f(8192, 8, 256) == (256 * 32 + 256) * 4     # 32 tiles of 256 tokens
+    assert f(32768, 8, 32) == (32 * 32 + 32) * 4       # 32 tiles of 1024 tokens
+    assert f(1, 1, 1024) == (1024 * 4 + 1024) * 4      # one tile, pitch 4
 
 
 def _expand(lib, T, H, k, mode, cap, x=FAKE, out=FAKE, scales=FAKE, pos=FAKE):

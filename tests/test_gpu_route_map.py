@@ -60,6 +60,9 @@ def test_route_plain_shapes(T, E, k, score):
 @pytest.mark.parametrize("E,n_groups,topk_groups,group_topn,k", [
     (256, 8, 4, 2, 8), (64, 8, 3, 1, 5), (16, 4, 2, 2, 3), (128, 4, 2, 3, 6),
     (512, 8, 2, 2, 8), (1024, 16, 4, 2, 8), (256, 2, 1, 2, 4), (256, 4, 4, 2, 8),
+    # group sizes spanning 1/4 lane .. 32 lanes, group_topn 1 and 2, k 3..8
+    (64, 8, 3, 1, 4), (128, 4, 2, 2, 6), (128, 2, 1, 2, 8), (32, 16, 4, 2, 5),
+    (64, 16, 8, 2, 3), (256, 64, 8, 2, 8), (256, 32, 4, 2, 8), (256, 16, 4, 1, 7),
 ])
 def test_route_group_limited(E, n_groups, topk_groups, group_topn, k):
     rng = np.random.default_rng(E + n_groups * 10 + k)
