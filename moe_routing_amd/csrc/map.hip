@@ -3,9 +3,9 @@
 // ops of TileKernels' moe/ module ("刚刚！DeepSeek开源高性能GPU算子库TileKernels",
 // item moe/).
 //
-// Tokens are cut into tiles of 32*S tokens (S sub-tiles of 32).  Two launches
-// at the usual sizes, no atomics on global memory, so every output is a pure
-// function of topk_idx:
+// Tokens are cut into tiles of 32*S <= 256 tokens (S sub-tiles of 32), one
+// token per thread.  Two launches at the usual sizes, no atomics on global
+// memory, so every output is a pure function of topk_idx:
 //   1. count  one workgroup per tile: LDS histogram of the tile's local
 //             routes -> cnt[e][tile] (expert-major) in the workspace
 //   2. place  one workgroup per tile: per expert, the sum over all tiles
@@ -14,7 +14,9 @@
 //             (expert, sub-tile) in LDS ranks the tile's tokens:
 //               pos = offsets[e] + before[e] + (tokens of e in earlier
 //                     sub-tiles) + popcount(bits below t in t's sub-tile)
-// When there are many tiles, a third launch (scan, between the two) turns the
+// The place kernel issues all its global loads (its tokens' ids, the count
+// rows) before any of the dependent work, so their latencies overlap.  When
+// the count matrix is large, a third launch (scan, between the two) turns the
 // counts into per-tile prefixes once, so that place reads one column instead
 // of a whole row per expert.
 // Ranks follow token order, which is the stable order because a token is
@@ -25,8 +27,8 @@ namespace {
 
 constexpr int kSub = 32;               // tokens per sub-tile (one mask word)
 constexpr int kThreads = 256;          // threads of the count and place kernels
-constexpr int kTargetTiles = 32;       // tiles aimed for, for parallelism
-constexpr int kMaxFusedTiles = 64;     // beyond this, prefixes come from the scan kernel
+constexpr int kMaxSub = kThreads / kSub;  // one token per thread: tiles <= 256 tokens
+constexpr int kMaxFusedInts = 32768;   // count matrix read whole by each place workgroup
 constexpr int kLdsWords = 12288;       // place kernel LDS budget (48 KiB)
 constexpr int kScanThreads = 1024;
 
@@ -42,13 +44,13 @@ __host__ inline Tiling tiling(int T, int n_local)
 {
     Tiling g{};
     int s_max = (kLdsWords - n_local) / (2 * n_local);  // mask + before words per tile
-    s_max = s_max < 1 ? 1 : (s_max > 64 ? 64 : s_max);
-    int s = (T + kSub * kTargetTiles - 1) / (kSub * kTargetTiles);
+    s_max = s_max < 1 ? 1 : (s_max > kMaxSub ? kMaxSub : s_max);
+    const int s = (T + kSub - 1) / kSub;                 // no more sub-tiles than tokens need
     g.S = s < 1 ? 1 : (s > s_max ? s_max : s);
     g.tile = g.S * kSub;
     g.n_tiles = T > 0 ? (T + g.tile - 1) / g.tile : 0;
     g.pitch = (g.n_tiles + 3) & ~3;
-    g.fused = g.n_tiles <= kMaxFusedTiles;
+    g.fused = static_cast<int64_t>(g.pitch) * n_local <= kMaxFusedInts;
     return g;
 }
 
@@ -78,14 +80,13 @@ __global__ __launch_bounds__(kThreads) void map_count_kernel(
 {
     extern __shared__ int32_t hist[];
     const int nl = hi - lo;
+    const int t = blockIdx.x * tile_tokens + threadIdx.x;
+    const bool mine = threadIdx.x < tile_tokens && t < T;
+    int e[KMAX];
+    if (mine) load_local_ids<KMAX>(idx, t, k, lo, hi, e);
     for (int i = threadIdx.x; i < nl; i += kThreads) hist[i] = 0;
     __syncthreads();
-    const int t0 = blockIdx.x * tile_tokens;
-    for (int tl = threadIdx.x; tl < tile_tokens; tl += kThreads) {
-        const int t = t0 + tl;
-        if (t >= T) break;
-        int e[KMAX];
-        load_local_ids<KMAX>(idx, t, k, lo, hi, e);
+    if (mine) {
 #pragma unroll
         for (int j = 0; j < KMAX; ++j)
             if (e[j] >= 0) atomicAdd(&hist[e[j]], 1);
@@ -158,6 +159,13 @@ __global__ __launch_bounds__(kThreads) void map_place_kernel(
     int32_t* base = reinterpret_cast<int32_t*>(lds + 2 * nl * S);  // [nl]
     const int tile = blockIdx.x;
     const int tile_tokens = S * kSub;
+    const int tl = threadIdx.x;
+    const int t = tile * tile_tokens + tl;
+    const bool mine = tl < tile_tokens && t < T;
+
+    // 0. this thread's token: its local expert ids (loads issued first)
+    int e[KMAX];
+    if (mine) load_local_ids<KMAX>(idx, t, k, lo, hi, e);
 
     // 1. per expert: total over all tiles, sum over the tiles before this one
     //    (this thread owns the ept consecutive experts [e0, e0 + ept))
@@ -165,9 +173,9 @@ __global__ __launch_bounds__(kThreads) void map_place_kernel(
     const int e0 = threadIdx.x * ept;
     int32_t my_total = 0;
     for (int i = 0; i < ept; ++i) {
-        const int e = e0 + i;
-        if (e >= nl) break;
-        const int32_t* row = cnt + static_cast<size_t>(e) * pitch;
+        const int ex = e0 + i;
+        if (ex >= nl) break;
+        const int32_t* row = cnt + static_cast<size_t>(ex) * pitch;
         int32_t tot = 0, bef = 0;
         if (fused) {
             for (int c = 0; c < n_tiles; c += 4) {
@@ -177,72 +185,63 @@ __global__ __launch_bounds__(kThreads) void map_place_kernel(
                        (c + 2 < tile ? v.z : 0) + (c + 3 < tile ? v.w : 0);
             }
         } else {
-            tot = totals[e];
+            tot = totals[ex];
             bef = row[tile];
         }
-        base[e] = bef;
+        base[ex] = bef;
         my_total += tot;
         // keep the expert's total until the scan below has produced offsets
-        before_sub[e] = static_cast<uint32_t>(tot);
+        before_sub[ex] = static_cast<uint32_t>(tot);
     }
+    for (int i = threadIdx.x; i < nl * S; i += kThreads) mask[i] = 0;
     __syncthreads();
-    // 2. offsets: exclusive scan of the totals over experts
+
+    // 2. bit masks per (expert, sub-tile); offsets = exclusive scan of totals
+    if (mine) {
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+            if (e[j] >= 0) atomicOr(&mask[e[j] * S + tl / kSub], 1u << (tl % kSub));
+    }
     int32_t grand = 0;
-    int32_t run = block_exclusive_scan(my_total, wave_sums, &grand);
+    int32_t run = block_exclusive_scan(my_total, wave_sums, &grand);   // syncs the block
     for (int i = 0; i < ept; ++i) {
-        const int e = e0 + i;
-        if (e >= nl) break;
-        const int32_t tot = static_cast<int32_t>(before_sub[e]);
+        const int ex = e0 + i;
+        if (ex >= nl) break;
+        const int32_t tot = static_cast<int32_t>(before_sub[ex]);
         if (tile == 0) {
-            counts[e] = tot;
-            offsets[e] = run;
+            counts[ex] = tot;
+            offsets[ex] = run;
         }
-        base[e] += run;
+        base[ex] += run;
         run += tot;
     }
     if (tile == 0 && threadIdx.x == 0) offsets[nl] = grand;
     __syncthreads();
 
-    // 3. rank the tile's tokens per expert: bit masks per (expert, sub-tile)
-    for (int i = threadIdx.x; i < nl * S; i += kThreads) mask[i] = 0;
-    __syncthreads();
-    const int t0 = tile * tile_tokens;
-    for (int tl = threadIdx.x; tl < tile_tokens; tl += kThreads) {
-        const int t = t0 + tl;
-        if (t >= T) break;
-        int e[KMAX];
-        load_local_ids<KMAX>(idx, t, k, lo, hi, e);
-#pragma unroll
-        for (int j = 0; j < KMAX; ++j)
-            if (e[j] >= 0) atomicOr(&mask[e[j] * S + tl / kSub], 1u << (tl % kSub));
-    }
-    __syncthreads();
+    // 3. tokens of each expert in the earlier sub-tiles of this tile
     for (int ex = threadIdx.x; ex < nl; ex += kThreads) {
         uint32_t r = 0;
-        for (int s = 0; s < S; ++s) {
-            before_sub[ex * S + s] = r;
-            r += __popc(mask[ex * S + s]);
+        for (int sb = 0; sb < S; ++sb) {
+            before_sub[ex * S + sb] = r;
+            r += __popc(mask[ex * S + sb]);
         }
     }
     __syncthreads();
-    for (int tl = threadIdx.x; tl < tile_tokens; tl += kThreads) {
-        const int t = t0 + tl;
-        if (t >= T) break;
-        int e[KMAX];
-        load_local_ids<KMAX>(idx, t, k, lo, hi, e);
-        const uint32_t below = (1u << (tl % kSub)) - 1u;
-        const int s = tl / kSub;
+
+    // 4. positions
+    if (!mine) return;
+    const uint32_t below = (1u << (tl % kSub)) - 1u;
+    const int sb = tl / kSub;
 #pragma unroll
-        for (int j = 0; j < KMAX; ++j) {
-            if (j >= k) break;
-            int32_t p = -1;
-            if (e[j] >= 0) {
-                const int w = e[j] * S + s;
-                p = base[e[j]] + static_cast<int32_t>(before_sub[w] + __popc(mask[w] & below));
-                if (row_src != nullptr) row_src[p] = t;
-            }
-            pos[static_cast<size_t>(t) * k + j] = p;
+    for (int j = 0; j < KMAX; ++j) {
+        if (j >= k) break;
+        int32_t p = -1;
+        if (e[j] >= 0) {
+            const int w = e[j] * S + sb;
+            p = base[e[j]] + static_cast<int32_t>(before_sub[w] + __popc(mask[w] & below));
+            if (row_src != nullptr) row_src[p] = t;
         }
+        pos[static_cast<size_t>(t) * k + j] = p;
     }
 }
 

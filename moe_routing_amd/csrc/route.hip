@@ -239,8 +239,10 @@ __global__ __launch_bounds__(tk::kBlock) void route_kernel(RouteArgs a)
 //    the winning lane's list;
 //  - a group's top-2 keys come from a butterfly over its lanes that merges
 //    (largest, second largest) pairs;
-//  - the weights re-read the k chosen logits (cache hits) instead of
-//    carrying scores through the rounds.
+//  - groups are ranked with one lane transpose and a ballot count when a
+//    group spans at least as many lanes as there are groups;
+//  - lane j fetches slot j's score from the lane holding it (ds_bpermute)
+//    for the weights.
 struct FastArgs {
     const float* logits;
     const float* bias;
@@ -307,15 +309,18 @@ __global__ __launch_bounds__(tk::kBlock) void route_fast_kernel(FastArgs a)
         }
     }
 
-    // selection keys (order-preserving uint32, 0 = not eligible)
+    // scores (what the weights use) and selection keys (order-preserving
+    // uint32, 0 = not eligible)
+    float sc[EPL];
     uint32_t key[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         float kf;
         if constexpr (SIGMOID) {
-            const float sv = pinned_sigmoid(x[i]);
-            kf = has_bias ? sv + b[i] : sv;
+            sc[i] = pinned_sigmoid(x[i]);
+            kf = has_bias ? sc[i] + b[i] : sc[i];
         } else {
+            sc[i] = x[i];
             kf = x[i];
         }
         key[i] = (e0 + i < a.E) ? order_key(kf) : 0u;
@@ -340,9 +345,21 @@ __global__ __launch_bounds__(tk::kBlock) void route_fast_kernel(FastArgs a)
         const uint32_t og = order_key(gs);
         const int g = lane / lpg;
         int rank = 0;
-        for (int gp = 0; gp < a.n_groups; ++gp) {
-            const uint32_t o = static_cast<uint32_t>(readlane_i(static_cast<int>(og), gp * lpg));
-            rank += (o > og || (o == og && gp < g)) ? 1 : 0;
+        if (lpg >= a.n_groups) {
+            // lane i of group g compares group g with group i; a ballot over
+            // the group's lanes counts the groups that beat g
+            const int i = lane & (lpg - 1);
+            const bool real = i < a.n_groups;
+            const uint32_t oi = static_cast<uint32_t>(__shfl(static_cast<int>(og), (real ? i : 0) * lpg));
+            const bool beats = real && (oi > og || (oi == og && i < g));
+            const uint64_t bal = __ballot(beats);
+            const uint64_t seg = (lpg == 64) ? ~0ull : (((1ull << lpg) - 1ull) << (g * lpg));
+            rank = __popcll(bal & seg);
+        } else {
+            for (int gp = 0; gp < a.n_groups; ++gp) {
+                const uint32_t o = static_cast<uint32_t>(readlane_i(static_cast<int>(og), gp * lpg));
+                rank += (o > og || (o == og && gp < g)) ? 1 : 0;
+            }
         }
         if (rank >= a.topk_groups) {
 #pragma unroll
@@ -350,41 +367,53 @@ __global__ __launch_bounds__(tk::kBlock) void route_fast_kernel(FastArgs a)
         }
     }
 
-    // per-lane list, sorted descending; ties keep the lower expert first
-    uint64_t c[EPL];
+    // per-lane list, sorted descending; ties keep the lower expert first.
+    // Sorted as 64-bit (key << 32 | EPL-1-i) composites, then split into the
+    // keys and a packed list of 2-bit local indices, head in the low bits.
+    uint32_t lk[EPL];
+    uint32_t li_packed = 0;
+    {
+        uint64_t c[EPL];
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) c[i] = (static_cast<uint64_t>(key[i]) << 32) | (EPL - 1 - i);
-    if constexpr (EPL == 2) {
-        cas_desc(c[0], c[1]);
-    } else if constexpr (EPL == 4) {
-        cas_desc(c[0], c[1]); cas_desc(c[2], c[3]);
-        cas_desc(c[0], c[2]); cas_desc(c[1], c[3]);
-        cas_desc(c[1], c[2]);
+        for (int i = 0; i < EPL; ++i) c[i] = (static_cast<uint64_t>(key[i]) << 32) | (EPL - 1 - i);
+        if constexpr (EPL == 2) {
+            cas_desc(c[0], c[1]);
+        } else if constexpr (EPL == 4) {
+            cas_desc(c[0], c[1]); cas_desc(c[2], c[3]);
+            cas_desc(c[0], c[2]); cas_desc(c[1], c[3]);
+            cas_desc(c[1], c[2]);
+        }
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            lk[i] = static_cast<uint32_t>(c[i] >> 32);
+            li_packed |= (EPL - 1 - static_cast<uint32_t>(c[i] & 3u)) << (2 * i);
+        }
     }
 
     int my_e = 0;
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-        const uint32_t head = static_cast<uint32_t>(c[0] >> 32);
-        const uint32_t m = tk::max_wave_u32(head);
-        const uint64_t won = __ballot(head == m);
+        const uint32_t m = tk::max_wave_u32(lk[0]);
+        const uint64_t won = __ballot(lk[0] == m);
         const int wl = tk::uniform(__ffsll(static_cast<long long>(won)) - 1);
-        const int li = EPL - 1 - readlane_i(static_cast<int>(static_cast<uint32_t>(c[0])), wl);
-        const int e = wl * EPL + li;
+        const int e = wl * EPL + readlane_i(static_cast<int>(li_packed & 3u), wl);
         if (lane == j) my_e = e;
         if (lane == wl) {
 #pragma unroll
-            for (int i = 0; i + 1 < EPL; ++i) c[i] = c[i + 1];
-            c[EPL - 1] = 0;
+            for (int i = 0; i + 1 < EPL; ++i) lk[i] = lk[i + 1];
+            lk[EPL - 1] = 0;
+            li_packed >>= 2;
         }
     }
 
-    // weights over the chosen experts, sums in slot order
+    // weights over the chosen experts, sums in slot order; lane j fetches
+    // the score of its expert from the lane that holds it
+    const int src_lane = my_e / EPL, src_i = my_e % EPL;
     float sv = 0.f;
-    if (lane < K) {
-        const float xv = row[min(max(my_e, 0), a.E - 1)];
-        sv = xv;
-        if constexpr (SIGMOID) sv = pinned_sigmoid(xv);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const float v = __shfl(sc[i], src_lane);
+        if (i == src_i) sv = v;
     }
     float z = 0.f, v0 = 0.f;
     if constexpr (SIGMOID) {

@@ -119,7 +119,7 @@ def test_map_workspace_bytes(lib):
     f = lib.tk_map_workspace_bytes
     assert f(0, 8, 256) == 0
     assert f(8192, 8, 256) == (256 * 32 + 256) * 4     # 32 tiles of 256 tokens
-    assert f(32768, 8, 32) == (32 * 32 + 32) * 4       # 32 tiles of 1024 tokens
+    assert f(32768, 8, 32) == (32 * 128 + 32) * 4      # 128 tiles of 256 tokens
     assert f(1, 1, 1024) == (1024 * 4 + 1024) * 4      # one tile, pitch 4
 
 
