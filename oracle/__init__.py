@@ -62,6 +62,14 @@ def _declare(L: ctypes.CDLL) -> ctypes.CDLL:
     L.orc_standin.restype = None
     L.orc_reduce.argtypes = [vp, i64, vp, vp, i32, i32, i32, vp]
     L.orc_reduce.restype = i32
+    L.orc_quant_f32_row.argtypes = [vp, i32, vp, vp]
+    L.orc_quant_f32_row.restype = None
+    L.orc_row_weights.argtypes = [vp, vp, i32, i32, i64, vp]
+    L.orc_row_weights.restype = None
+    L.orc_swiglu_quant.argtypes = [vp, i64, i32, vp, vp, vp]
+    L.orc_swiglu_quant.restype = i32
+    L.orc_swiglu_f32.argtypes = [vp, i64, i32, vp, vp]
+    L.orc_swiglu_f32.restype = i32
     for name in ("orc_e4m3_from_f32_n", "orc_bf16_from_f32_n", "orc_bf16_from_f64_n",
                  "orc_sigmoid_f32_n", "orc_exp_f32_n"):
         getattr(L, name).argtypes = [vp, i64, vp]
@@ -218,3 +226,46 @@ def reduce(y, pos, w):
     if rc != 0:
         raise ValueError("oracle reduce: unsupported arguments")
     return out
+
+
+# ------------------------------------------------------- next: SwiGLU + FP8 --
+def quant_f32_row(a):
+    """1x128 E4M3 quantisation of fp32 rows ((..., n), n % 128 == 0)."""
+    a = _c(a, np.float32)
+    n = a.shape[-1]
+    flat = a.reshape(-1, n)
+    q = np.empty(flat.shape, np.uint8)
+    sc = np.empty((flat.shape[0], n // 128), np.float32)
+    for i in range(flat.shape[0]):
+        lib().orc_quant_f32_row(_p(flat[i]), n, _p(q[i]), _p(sc[i]))
+    return q.reshape(a.shape), sc.reshape(a.shape[:-1] + (n // 128,))
+
+
+def row_weights(pos, w, rows: int):
+    pos = _c(pos, np.int32)
+    w = _c(w, np.float32)
+    T, k = pos.shape
+    out = np.empty(rows, np.float32)
+    lib().orc_row_weights(_p(pos), _p(w), T, k, rows, _p(out))
+    return out
+
+
+def swiglu_f32(h, I: int, row_w=None):
+    h = _c(h, np.uint16)
+    rows = h.shape[0]
+    a = np.empty((rows, I), np.float32)
+    rw = None if row_w is None else _c(row_w, np.float32)
+    if lib().orc_swiglu_f32(_p(h), rows, I, _p(rw), _p(a)) != 0:
+        raise ValueError("oracle swiglu: unsupported arguments")
+    return a
+
+
+def swiglu_quant(h, I: int, row_w=None):
+    h = _c(h, np.uint16)
+    rows = h.shape[0]
+    q = np.empty((rows, I), np.uint8)
+    sc = np.empty((rows, I // 128), np.float32)
+    rw = None if row_w is None else _c(row_w, np.float32)
+    if lib().orc_swiglu_quant(_p(h), rows, I, _p(rw), _p(q), _p(sc)) != 0:
+        raise ValueError("oracle swiglu_quant: unsupported arguments")
+    return q, sc

@@ -451,6 +451,91 @@ int orc_reduce(const uint16_t* y, int64_t rows, const int32_t* pos, const float*
     return 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Per-token 1x128 FP8 quantisation of one row of n fp32 values (the same    */
+/* codec as orc_quant_row, on fp32 input).  n must be a multiple of 128.     */
+/*   amax  = max |a| over the block, at least 1e-4f                          */
+/*   scale = RN32(amax / 448);  q_c = E4M3(RN32(a_c / scale))                */
+/* ------------------------------------------------------------------------ */
+void orc_quant_f32_row(const float* a, int n, uint8_t* q, float* scales)
+{
+    for (int b = 0; b < n / 128; ++b) {
+        float amax = 0.0f;
+        for (int c = b * 128; c < b * 128 + 128; ++c) {
+            const float m = fabsf(a[c]);
+            if (m > amax) amax = m;
+        }
+        if (amax < 1e-4f) amax = 1e-4f;
+        const float scale = amax / 448.0f;
+        scales[b] = scale;
+        for (int c = b * 128; c < b * 128 + 128; ++c) q[c] = orc_e4m3_from_f32(a[c] / scale);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Weight of each expanded row: row_w[pos[t,j]] = w[t,j] for every route     */
+/* with 0 <= pos < rows; rows no route points at keep 0.                     */
+/* ------------------------------------------------------------------------ */
+void orc_row_weights(const int32_t* pos, const float* w, int T, int k, int64_t rows, float* row_w)
+{
+    for (int64_t r = 0; r < rows; ++r) row_w[r] = 0.0f;
+    for (int t = 0; t < T; ++t)
+        for (int j = 0; j < k; ++j) {
+            const int64_t r = pos[(size_t)t * k + j];
+            if (r >= 0 && r < rows) row_w[r] = w[(size_t)t * k + j];
+        }
+}
+
+/* ------------------------------------------------------------------------ */
+/* SwiGLU activation fused with per-token 1x128 FP8 quantisation (the        */
+/* "SwiGLU + FP8 quantisation" fusion of TileKernels' quant/ module), with   */
+/* an optional per-row weight (the routing weight of the expanded row).      */
+/* Row r of h holds 2*I bf16 values: gate g = h[r, 0..I), up u = h[r, I..2I).*/
+/* In fp32, one IEEE operation per step:                                     */
+/*   s = sigmoid(g)  (the pinned orc_sigmoid_f32)                            */
+/*   a = RN(RN(g * s) * u);  weighted: a = RN(a * row_w[r])                  */
+/* then a is quantised with orc_quant_f32_row into out[r] (I codes) and      */
+/* scales[r] (I/128).  I must be a multiple of 128.                          */
+/* ------------------------------------------------------------------------ */
+int orc_swiglu_quant(const uint16_t* h, int64_t rows, int I, const float* row_w, uint8_t* out,
+                     float* scales)
+{
+    if (rows < 0 || I < 128 || I % 128 != 0) return -1;
+    float* a = (float*)malloc(sizeof(float) * (size_t)I);
+    if (!a) return -1;
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint16_t* hr = h + (size_t)r * 2 * I;
+        for (int c = 0; c < I; ++c) {
+            const float g = orc_bf16_to_f32(hr[c]);
+            const float u = orc_bf16_to_f32(hr[I + c]);
+            const float s = orc_sigmoid_f32(g);
+            float v = (g * s) * u;
+            if (row_w) v = v * row_w[r];
+            a[c] = v;
+        }
+        orc_quant_f32_row(a, I, out + (size_t)r * I, scales + (size_t)r * (I / 128));
+    }
+    free(a);
+    return 0;
+}
+
+/* The fp32 activations alone (before quantisation), for the pins. */
+int orc_swiglu_f32(const uint16_t* h, int64_t rows, int I, const float* row_w, float* a)
+{
+    if (rows < 0 || I < 1) return -1;
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint16_t* hr = h + (size_t)r * 2 * I;
+        for (int c = 0; c < I; ++c) {
+            const float g = orc_bf16_to_f32(hr[c]);
+            const float u = orc_bf16_to_f32(hr[I + c]);
+            float v = (g * orc_sigmoid_f32(g)) * u;
+            if (row_w) v = v * row_w[r];
+            a[(size_t)r * I + c] = v;
+        }
+    }
+    return 0;
+}
+
 /* Element-wise helpers over arrays, for the codec pins. */
 void orc_e4m3_from_f32_n(const float* v, int64_t n, uint8_t* q)
 {
