@@ -54,6 +54,8 @@ def _declare(L: ctypes.CDLL) -> ctypes.CDLL:
     L.orc_route.restype = i32
     L.orc_map.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]
     L.orc_map.restype = i32
+    L.orc_map_aligned.argtypes = [vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]
+    L.orc_map_aligned.restype = i32
     L.orc_expand.argtypes = [vp, i32, i32, i32, vp, i32, i64, vp, vp]
     L.orc_expand.restype = i32
     L.orc_quant_row.argtypes = [vp, i32, vp, vp]
@@ -175,6 +177,24 @@ def map_routes(topk_idx, E: int, lo: int = 0, hi: int | None = None, with_row_sr
     if with_row_src:
         row_src = row_src[: int(offsets[-1])].copy()
     return counts, offsets, pos, row_src
+
+
+def map_aligned(topk_idx, E: int, lo: int = 0, hi: int | None = None, align: int = 1):
+    """Map with expert segments padded to multiples of `align` rows; row_src
+    covers all offsets[-1] rows, -1 on padding rows."""
+    topk_idx = _c(topk_idx, np.int32)
+    T, k = topk_idx.shape
+    hi = E if hi is None else hi
+    nl = hi - lo
+    counts = np.empty(nl, np.int32)
+    offsets = np.empty(nl + 1, np.int32)
+    pos = np.empty((T, k), np.int32)
+    row_src = np.empty(T * k + nl * (align - 1), np.int32)
+    rc = lib().orc_map_aligned(_p(topk_idx), T, k, E, lo, hi, align, _p(counts), _p(offsets),
+                               _p(pos), _p(row_src))
+    if rc != 0:
+        raise ValueError("oracle map_aligned: unsupported arguments")
+    return counts, offsets, pos, row_src[: int(offsets[-1])].copy()
 
 
 def quant_row(x_row):

@@ -351,6 +351,57 @@ int orc_map(const int32_t* topk_idx, int T, int k, int E, int lo, int hi,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Map with expert segments aligned for a grouped GEMM: expert e's rows      */
+/* start at a multiple of `align` and its segment holds                       */
+/* roundup(counts[e], align) rows:                                           */
+/*   offsets[0] = 0, offsets[e+1] = offsets[e] + roundup(counts[e], align)   */
+/*   pos[t,j]   = offsets[e] + (number of earlier tokens routed to e)         */
+/*   row_src[r] = t for the rows routes land on, -1 for padding rows, for    */
+/*                r < offsets[hi-lo]                                          */
+/* align = 1 is orc_map.                                                     */
+/* ------------------------------------------------------------------------ */
+int orc_map_aligned(const int32_t* topk_idx, int T, int k, int E, int lo, int hi, int align,
+                    int32_t* counts, int32_t* offsets, int32_t* pos, int32_t* row_src)
+{
+    if (T < 0 || k < 1 || E < 1 || lo < 0 || hi > E || lo >= hi || align < 1) return -1;
+    const int nl = hi - lo;
+    for (int i = 0; i < nl; ++i) counts[i] = 0;
+    for (int t = 0; t < T; ++t)
+        for (int j = 0; j < k; ++j) {
+            const int32_t e = topk_idx[(size_t)t * k + j];
+            int first = 1;
+            for (int jj = 0; jj < j; ++jj)
+                if (topk_idx[(size_t)t * k + jj] == e) first = 0;
+            if (first && e >= lo && e < hi) counts[e - lo] += 1;
+        }
+    offsets[0] = 0;
+    for (int i = 0; i < nl; ++i) {
+        const int32_t padded = ((counts[i] + align - 1) / align) * align;
+        offsets[i + 1] = offsets[i] + padded;
+    }
+    if (row_src)
+        for (int32_t r = 0; r < offsets[nl]; ++r) row_src[r] = -1;
+    int32_t* cursor = (int32_t*)calloc((size_t)nl, sizeof(int32_t));
+    if (!cursor) return -1;
+    for (int t = 0; t < T; ++t)
+        for (int j = 0; j < k; ++j) {
+            const int32_t e = topk_idx[(size_t)t * k + j];
+            int first = 1;
+            for (int jj = 0; jj < j; ++jj)
+                if (topk_idx[(size_t)t * k + jj] == e) first = 0;
+            int32_t p = -1;
+            if (first && e >= lo && e < hi) {
+                p = offsets[e - lo] + cursor[e - lo];
+                cursor[e - lo] += 1;
+                if (row_src) row_src[p] = t;
+            }
+            pos[(size_t)t * k + j] = p;
+        }
+    free(cursor);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Per-token 1x128 FP8 quantisation of one row of H bf16 values.             */
 /* For each block b of 128 consecutive columns:                              */
 /*   amax  = max |x| over the block (bf16 -> fp32 is exact), at least 1e-4f   */

@@ -77,3 +77,42 @@ def test_map_repeated_id_routed_once():
     assert offsets.tolist() == [0, 1, 3, 4, 5]
     assert pos.tolist() == [[4, -1, 1], [2, 3, -1], [0, -1, -1]]
     assert row_src.tolist() == [2, 0, 1, 1, 0]
+
+
+def _torch_map_aligned(idx: np.ndarray, lo: int, hi: int, align: int):
+    """The torch reference above, with each expert's segment padded to a
+    multiple of `align` rows (padding rows have no source token: -1)."""
+    counts, _, pos_plain, row_src_plain = _torch_map(idx, lo, hi)
+    c = torch.from_numpy(counts.astype(np.int64))
+    padded = (c + align - 1) // align * align
+    offsets = torch.cat([torch.zeros(1, dtype=torch.int64), torch.cumsum(padded, 0)])
+    plain_off = torch.cat([torch.zeros(1, dtype=torch.int64), torch.cumsum(c, 0)])
+    T, k = idx.shape
+    flat = torch.from_numpy(idx.reshape(-1).astype(np.int64))
+    p = torch.from_numpy(pos_plain.reshape(-1).astype(np.int64))
+    valid = p >= 0
+    e = torch.where(valid, flat - lo, torch.zeros_like(flat))
+    pos = torch.where(valid, p - plain_off[e] + offsets[e], torch.full_like(p, -1))
+    row_src = torch.full((int(offsets[-1]),), -1, dtype=torch.int64)
+    row_src[pos[valid]] = torch.arange(T * k)[valid] // k
+    return counts, offsets.numpy(), pos.view(T, k).numpy(), row_src.numpy()
+
+
+@pytest.mark.parametrize("T,E,k,lo,hi,align", [
+    (37, 16, 2, 0, 16, 1), (500, 64, 6, 0, 64, 128), (1000, 256, 8, 0, 256, 128),
+    (1000, 256, 8, 32, 64, 64), (333, 32, 4, 5, 9, 7), (0, 8, 2, 0, 8, 16), (64, 16, 2, 0, 16, 3),
+])
+def test_map_aligned_matches_torch(T, E, k, lo, hi, align):
+    rng = np.random.default_rng(T + E + k + lo + align)
+    idx = synth.random_routing(rng, T, E, k)
+    got = oracle.map_aligned(idx, E, lo, hi, align)
+    ref = _torch_map_aligned(idx, lo, hi, align)
+    for g, r, name in zip(got, ref, ("counts", "offsets", "pos", "row_src")):
+        assert np.array_equal(g, r), name
+    counts, offsets, pos, row_src = got
+    assert np.all(offsets % align == 0)
+    assert np.all(np.diff(offsets) >= counts) and np.all(np.diff(offsets) - counts < align)
+    if align == 1:
+        plain = oracle.map_routes(idx, E, lo, hi)
+        for g, r in zip(got, plain):
+            assert np.array_equal(g, r)
