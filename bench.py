@@ -18,6 +18,10 @@ the path: the reduce consumes a fixed expert-output tensor.
 Prints ONE JSON line: routed tokens/s (value), the pipeline's algorithmic
 HBM GB/s, per-kernel times from HIP events recorded on the launch stream, the
 roofline of the dominant kernel (the reduce) and the CPU oracle's rate.
+Steps beyond the routing path (next_rows) are timed separately on the same
+data and do not enter value: SwiGLU + 1x128 FP8 quantisation of the 65536
+expanded rows at the DeepSeek-V3 expert width I = 2048, weighted by the
+routing weights through the step's map.
 """
 from __future__ import annotations
 
@@ -107,6 +111,48 @@ def cpu_baseline(inputs, reps: int = 2) -> dict:
             "sample": f"{reps} full steps (T={T} each) of route+map+expand(FP8)+reduce through the "
                       f"single-threaded C oracle, mean per step: route+map {t_rm / reps:.2f}s, "
                       f"expand {t_ex / reps:.2f}s, reduce {t_rd / reps:.2f}s"}
+
+
+# SwiGLU + FP8 row: the defined arithmetic per output element, one IEEE fp32
+# operation per rounding: sigmoid 17 (negate, two range tests, y*log2e, rint,
+# two Cody-Waite fmas, seven Horner fmas, ldexp, 1+E, division), g*s, *u, *w,
+# |a|, block max, quotient, E4M3 encode.
+SWIGLU_I = 2048
+SWIGLU_OPS_PER_ELEM = 24
+PEAK_VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12    # fp32 lane-operations per second, no packing
+
+
+def bench_swiglu(tk, torch, y, n_rows, row_src, pos, w, steps):
+    """SwiGLU + 1x128 FP8 over the step's expanded rows (weighted)."""
+    I = SWIGLU_I
+    h = y.view(-1)[: R * 2 * I].view(R, 2 * I)      # N(0,1) bf16 rows of width 2*I
+    q = torch.empty((R, I), dtype=torch.uint8, device=y.device)
+    s = torch.empty((R, I // 128), dtype=torch.float32, device=y.device)
+
+    def call():
+        tk.tk_swiglu_quant(h, n_rows, row_src, pos, w, q, s)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        call()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / steps
+    nbytes = R * 2 * I * 2 + R * I + R * (I // 128) * 4 + R * 4 + T * K * 8
+    ops = R * I * SWIGLU_OPS_PER_ELEM
+    return {"workload": f"{R} expanded rows of the step's routing, I={I} (gate|up bf16 -> "
+                        "E4M3 + fp32 1x128 scales), routing weights applied",
+            "us_per_launch": round(us, 2), "hbm_gbps": round(nbytes / us / 1e3, 1),
+            "algorithmic_bytes": nbytes,
+            "roofline": {"kernel": "swiglu_quant_kernel<true>", "bound": "alu",
+                         "achieved": round(ops / us / 1e6, 2), "peak": round(PEAK_VALU_TOPS, 2),
+                         "unit": "Top/s", "frac": round(ops / us / 1e6 / PEAK_VALU_TOPS, 4),
+                         "ops_per_element": SWIGLU_OPS_PER_ELEM}}
 
 
 def main() -> int:
@@ -218,6 +264,9 @@ def main() -> int:
             b.copy_(a)
         torch.cuda.synchronize()
 
+    next_rows = {"swiglu_quant_fp8": bench_swiglu(tk, torch, y, offsets[E:], row_src, pos, w,
+                                                  args.steps)}
+
     ms_per_step = total_ms / args.steps
     value = T / (ms_per_step * 1e-3)
     gbps = BYTES["total"] / (ms_per_step * 1e-3) / 1e9
@@ -255,6 +304,7 @@ def main() -> int:
                      "traffic": traffic,
                      "algorithmic_bytes_per_launch": BYTES["reduce"]},
         "cpu_baseline": None,
+        "next_rows": next_rows,
     }
     if not args.no_cpu_baseline:
         inputs = (gate["logits"], gate["bias"], x_h, y_h, r)

@@ -10,6 +10,11 @@
  *                    optionally fused 1x128 FP8 E4M3 quant    scales])
  *   tk_reduce        weighted combine back to tokens        (rows, w -> out)
  *
+ * the next step after an expert's first grouped GEMM,
+ *
+ *   tk_swiglu_quant  SwiGLU + 1x128 FP8 quantisation        (rows -> codes,
+ *                    (+ routing weight)                        scales)
+ *
  * plus tk_expert_standin, a dequantise-and-scale harness kernel that stands in
  * for the expert computation in end-to-end tests.
  *
@@ -162,6 +167,28 @@ tk_status tk_map(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
                  int32_t* pos, int32_t* row_src, void* workspace, size_t workspace_bytes,
                  hipStream_t stream);
 
+/*
+ * tk_map_aligned -- tk_map with every expert's segment padded for an
+ * M-blocked grouped GEMM (the expert-contiguous layout a grouped GEMM such as
+ * DeepGEMM's m-grouped kernel reads, "DeepSeek 的 GPU 内核帝国…", section
+ * 第二层：DeepGEMM, kernel list; the "new GEMM layout" of DeepEP V2 in
+ * "剛剛，DeepSeek開始頻繁更新：Tile Kernels、DeepEP V2", EPv2 features):
+ *   offsets[0] = 0, offsets[e+1] = offsets[e] + roundup(counts[e], align)
+ *   pos[t,j]   = offsets[e] + number of tokens t' < t routed to e (or -1)
+ *   row_src[r] = source token of row r, -1 for a padding row, r < offsets[n_local]
+ * so every segment starts at a multiple of align.  align = 1 is tk_map.  The
+ * padded row count offsets[n_local] is at most T*k + n_local*(align-1), which
+ * is the capacity callers allocate for row_src and the expanded rows; that
+ * bound must fit in int32.  Padding rows are never written by
+ * tk_expand_quant nor read by tk_reduce.
+ *
+ * align  >= 1; the other arguments as for tk_map
+ */
+tk_status tk_map_aligned(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
+                         int32_t local_begin, int32_t local_end, int32_t align, int32_t* counts,
+                         int32_t* offsets, int32_t* pos, int32_t* row_src, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
 /* ----------------------------------------------------------------- expand */
 #define TK_EXPAND_BF16 0            /* rows are bitwise copies of the token */
 #define TK_EXPAND_FP8_E4M3_1X128 1  /* rows are 1x128-block FP8 E4M3 codes */
@@ -207,6 +234,45 @@ tk_status tk_expand_quant(const void* x_bf16, int32_t T, int32_t H, int32_t k,
  */
 tk_status tk_reduce(const void* y_bf16, int64_t rows, const int32_t* pos, const float* topk_w,
                     int32_t T, int32_t k, int32_t H, void* out_bf16, hipStream_t stream);
+
+/* ------------------------------------------------- SwiGLU + FP8 quant */
+/*
+ * tk_swiglu_quant -- SwiGLU activation fused with per-token 1x128 FP8 E4M3
+ * quantisation of expert rows, optionally applying each row's routing weight:
+ * the "SwiGLU + FP8 quantisation" fusion of TileKernels' quant/ module
+ * ("刚刚！DeepSeek开源高性能GPU算子库TileKernels", item quant/; "剛剛，DeepSeek
+ * 開始頻繁更新：Tile Kernels、DeepEP V2", feature list) and the weighted
+ * SwiGLU-to-FP8 helper of the DeepGEMM kernel list ("DeepSeek 的 GPU 内核帝国…",
+ * section 第二层：DeepGEMM).
+ *
+ * Per row r < n (n = *n_rows clamped to [0, rows_capacity], or rows_capacity
+ * when n_rows is NULL) and column c < I, in fp32 with one IEEE rounding per
+ * step:
+ *   g = h[r, c], u = h[r, I + c];  s = 1/(1 + E(-g)) (the pinned sigmoid of
+ *   tk_route);  a = RN(RN(g*s)*u);  weighted: a = RN(a * w_r)
+ * then per 128-column block: amax = max(max |a|, 1e-4), scale = RN(amax/448),
+ * out[r, c] = E4M3(RN(a / scale)) (OCP E4M3FN, nearest even, sign kept),
+ * scales[r, c/128] = scale.  Rows r >= n are not written.
+ * Activations that overflow fp32 (|g*u| beyond ~3.4e38) give unspecified codes.
+ * Weighted when row_src, pos and topk_w are all given (all NULL: unweighted):
+ * w_r = topk_w[t, j] for t = row_src[r] and the slot j with pos[t, j] == r
+ * (as written by tk_map), 0 if there is none.
+ *
+ * h_bf16        device, bf16 (rows_capacity, 2*I): gate columns then up
+ *               columns; 16-byte aligned
+ * rows_capacity rows of h, out and scales, >= 0
+ * n_rows        device, one int32 (e.g. offsets + n_local from tk_map), or NULL
+ * I             output columns, a positive multiple of 128
+ * row_src, pos, topk_w, T, k
+ *               device int32 (rows_capacity), int32 (T, k), fp32 (T, k): the
+ *               map and the routing weights; or all NULL
+ * out           device, E4M3 bytes (rows_capacity, I), 16-byte aligned
+ * scales        device, fp32 (rows_capacity, I/128)
+ */
+tk_status tk_swiglu_quant(const void* h_bf16, int64_t rows_capacity, const int32_t* n_rows,
+                          int32_t I, const int32_t* row_src, const int32_t* pos,
+                          const float* topk_w, int32_t T, int32_t k, void* out, float* scales,
+                          hipStream_t stream);
 
 /* -------------------------------------------------------- test harness */
 /*

@@ -8,9 +8,11 @@ step of the path runs in the library's HIP kernels; there is no fallback.
 
     tk_route(logits, bias, k, opts)            -> (topk_idx, topk_w)
     tk_map(topk_idx, E, local_begin, local_end) -> (counts, offsets, pos, row_src)
+    tk_map_aligned(topk_idx, E, local_begin, local_end, align) -> (counts, offsets, pos, row_src)
     tk_expand_quant(x, pos, mode, rows_capacity) -> (out, scales)
     tk_reduce(y, pos, topk_w)                  -> out
     tk_expert_standin(xq, scales, n_rows, mult) -> y
+    tk_swiglu_quant(h, I, n_rows, row_src, pos, topk_w) -> (out, scales)
 """
 from __future__ import annotations
 
@@ -78,12 +80,16 @@ def library() -> ctypes.CDLL:
         L.tk_map_workspace_bytes.restype = sz
         L.tk_map.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
         L.tk_map.restype = i32
+        L.tk_map_aligned.argtypes = [vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+        L.tk_map_aligned.restype = i32
         L.tk_expand_quant.argtypes = [vp, i32, i32, i32, vp, i32, vp, vp, i64, vp]
         L.tk_expand_quant.restype = i32
         L.tk_reduce.argtypes = [vp, i64, vp, vp, i32, i32, i32, vp, vp]
         L.tk_reduce.restype = i32
         L.tk_expert_standin.argtypes = [vp, vp, vp, i64, i32, f32, vp, vp]
         L.tk_expert_standin.restype = i32
+        L.tk_swiglu_quant.argtypes = [vp, i64, vp, i32, vp, vp, vp, i32, i32, vp, vp, vp]
+        L.tk_swiglu_quant.restype = i32
         _lib = L
     return _lib
 
@@ -140,6 +146,16 @@ def tk_map_workspace_bytes(T: int, k: int, n_local: int) -> int:
 def tk_map(topk_idx: torch.Tensor, E: int, local_begin: int = 0, local_end: int | None = None,
            counts=None, offsets=None, pos=None, row_src=None, workspace=None,
            want_row_src: bool = True):
+    return tk_map_aligned(topk_idx, E, local_begin, local_end, 1, counts, offsets, pos, row_src,
+                          workspace, want_row_src)
+
+
+def tk_map_aligned(topk_idx: torch.Tensor, E: int, local_begin: int = 0,
+                   local_end: int | None = None, align: int = 1, counts=None, offsets=None,
+                   pos=None, row_src=None, workspace=None, want_row_src: bool = True):
+    """Map with each expert's segment padded to a multiple of `align` rows.
+    row_src (when allocated here) holds T*k + n_local*(align-1) entries, the
+    largest padded row count."""
     _dev(topk_idx, "topk_idx", torch.int32, 2)
     T, k = topk_idx.shape
     local_end = E if local_end is None else local_end
@@ -149,18 +165,18 @@ def tk_map(topk_idx: torch.Tensor, E: int, local_begin: int = 0, local_end: int 
     offsets = torch.empty(max(nl, 0) + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
     pos = torch.empty((T, k), dtype=torch.int32, device=dev) if pos is None else pos
     if row_src is None and want_row_src:
-        row_src = torch.empty(T * k, dtype=torch.int32, device=dev)
+        row_src = torch.empty(T * k + max(nl, 0) * max(align - 1, 0), dtype=torch.int32, device=dev)
     need = tk_map_workspace_bytes(T, k, nl) if nl > 0 else 0
     if workspace is None:
-        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     for name, t in (("counts", counts), ("offsets", offsets), ("pos", pos)):
         _dev(t, name, torch.int32)
     if row_src is not None:
         _dev(row_src, "row_src", torch.int32)
     _dev(workspace, "workspace", torch.uint8)
-    _check("tk_map", library().tk_map(_ptr(topk_idx), T, k, E, local_begin, local_end,
-                                      _ptr(counts), _ptr(offsets), _ptr(pos), _ptr(row_src),
-                                      _ptr(workspace), workspace.numel(), _stream(topk_idx)))
+    _check("tk_map", library().tk_map_aligned(
+        _ptr(topk_idx), T, k, E, local_begin, local_end, align, _ptr(counts), _ptr(offsets),
+        _ptr(pos), _ptr(row_src), _ptr(workspace), workspace.numel(), _stream(topk_idx)))
     return counts, offsets, pos, row_src
 
 
@@ -220,3 +236,37 @@ def tk_expert_standin(xq: torch.Tensor, scales: torch.Tensor, n_rows: torch.Tens
     _check("tk_expert_standin", library().tk_expert_standin(
         _ptr(xq), _ptr(scales), _ptr(n_rows), cap, H, float(mult), _ptr(y), _stream(xq)))
     return y
+
+
+def tk_swiglu_quant(h: torch.Tensor, n_rows: torch.Tensor | None = None,
+                    row_src: torch.Tensor | None = None, pos: torch.Tensor | None = None,
+                    topk_w: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                    scales: torch.Tensor | None = None):
+    """SwiGLU (gate = first half of each row, up = second half) fused with
+    1x128 FP8 E4M3 quantisation; weighted by the routing weights when
+    row_src, pos and topk_w are given."""
+    _dev(h, "h", torch.bfloat16, 2)
+    cap, two_i = h.shape
+    if two_i % 2:
+        raise ValueError("h must have 2*I columns")
+    I = two_i // 2
+    if n_rows is not None:
+        _dev(n_rows, "n_rows", torch.int32)
+    T = k = 0
+    if pos is not None:
+        _dev(pos, "pos", torch.int32, 2)
+        T, k = pos.shape
+    if row_src is not None:
+        _dev(row_src, "row_src", torch.int32)
+    if topk_w is not None:
+        _dev(topk_w, "topk_w", torch.float32)
+    if out is None:
+        out = torch.empty((cap, I), dtype=torch.uint8, device=h.device)
+    if scales is None:
+        scales = torch.empty((cap, max(I // 128, 1)), dtype=torch.float32, device=h.device)
+    _dev(out, "out", torch.uint8)
+    _dev(scales, "scales", torch.float32)
+    _check("tk_swiglu_quant", library().tk_swiglu_quant(
+        _ptr(h), cap, _ptr(n_rows), I, _ptr(row_src), _ptr(pos), _ptr(topk_w), T, k,
+        _ptr(out), _ptr(scales), _stream(h)))
+    return out, scales

@@ -33,26 +33,6 @@ constexpr int kChunkFp8 = 1024;   // columns per wave step, FP8 mode (16 per lan
 constexpr int kChunkBf16 = 512;   // columns per wave step, bf16 mode (8 per lane)
 constexpr int kExpandWaves = 8;   // waves per workgroup (one token per workgroup)
 
-// x / scale for scale > 0.  The correction step maps x = -0 to +0 (the sum
-// +0 + -0 rounds to +0), so the sign of x is put back; for x != 0 the sign
-// is already right and copysign changes nothing.
-__device__ __forceinline__ float quotient(float x, float scale, float inv)
-{
-    const float q0 = x * inv;
-    const float r = __builtin_fmaf(-q0, scale, x);
-    return __builtin_copysignf(__builtin_fmaf(r, inv, q0), x);
-}
-
-// Four quotients -> four E4M3 codes (gfx950 hardware convert: OCP E4M3FN,
-// round to nearest even).  amax / RN(amax/448) can exceed 448 by one fp32
-// ulp; such values round to 448 like every value below 464.
-__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d)
-{
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
-    return static_cast<uint32_t>(w);
-}
-
 // Rows of token t: rows[j] for j < k, -1 where the route is skipped.
 template <int KMAX>
 __device__ __forceinline__ void token_rows(const int32_t* __restrict__ pos, int t, int k,
@@ -104,14 +84,14 @@ __global__ __launch_bounds__(tk::kWave * kExpandWaves) void expand_fp8_kernel(
         const float scale = amax / 448.0f;
         const float inv = 1.0f / scale;
         tk::u32x4 q;
-        q.x = pack_fp8x4(quotient(v[0], scale, inv), quotient(v[1], scale, inv),
-                         quotient(v[2], scale, inv), quotient(v[3], scale, inv));
-        q.y = pack_fp8x4(quotient(v[4], scale, inv), quotient(v[5], scale, inv),
-                         quotient(v[6], scale, inv), quotient(v[7], scale, inv));
-        q.z = pack_fp8x4(quotient(v[8], scale, inv), quotient(v[9], scale, inv),
-                         quotient(v[10], scale, inv), quotient(v[11], scale, inv));
-        q.w = pack_fp8x4(quotient(v[12], scale, inv), quotient(v[13], scale, inv),
-                         quotient(v[14], scale, inv), quotient(v[15], scale, inv));
+        q.x = tk::pack_fp8x4(tk::fp8_quotient(v[0], scale, inv), tk::fp8_quotient(v[1], scale, inv),
+                         tk::fp8_quotient(v[2], scale, inv), tk::fp8_quotient(v[3], scale, inv));
+        q.y = tk::pack_fp8x4(tk::fp8_quotient(v[4], scale, inv), tk::fp8_quotient(v[5], scale, inv),
+                         tk::fp8_quotient(v[6], scale, inv), tk::fp8_quotient(v[7], scale, inv));
+        q.z = tk::pack_fp8x4(tk::fp8_quotient(v[8], scale, inv), tk::fp8_quotient(v[9], scale, inv),
+                         tk::fp8_quotient(v[10], scale, inv), tk::fp8_quotient(v[11], scale, inv));
+        q.w = tk::pack_fp8x4(tk::fp8_quotient(v[12], scale, inv), tk::fp8_quotient(v[13], scale, inv),
+                         tk::fp8_quotient(v[14], scale, inv), tk::fp8_quotient(v[15], scale, inv));
         if (active) {
 #pragma unroll
             for (int j = 0; j < KMAX; ++j) {

@@ -21,6 +21,8 @@
 // of a whole row per expert.
 // Ranks follow token order, which is the stable order because a token is
 // routed to an expert at most once (repeats in a row are dropped).
+// tk_map_aligned pads every expert's segment to a multiple of `align` rows
+// (the layout an M-blocked grouped GEMM reads); tk_map is align = 1.
 #include "tk_internal.h"
 
 namespace {
@@ -147,7 +149,7 @@ __device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* wave
 template <int KMAX>
 __global__ __launch_bounds__(kThreads) void map_place_kernel(
     const int32_t* __restrict__ idx, int T, int k, int lo, int hi, int S, int n_tiles, int pitch,
-    int fused, const int32_t* __restrict__ cnt, const int32_t* __restrict__ totals,
+    int fused, int align, const int32_t* __restrict__ cnt, const int32_t* __restrict__ totals,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ pos,
     int32_t* __restrict__ row_src)
 {
@@ -189,14 +191,15 @@ __global__ __launch_bounds__(kThreads) void map_place_kernel(
             bef = row[tile];
         }
         base[ex] = bef;
-        my_total += tot;
+        my_total += (tot + align - 1) / align * align;   // the expert's segment, padded
         // keep the expert's total until the scan below has produced offsets
         before_sub[ex] = static_cast<uint32_t>(tot);
     }
     for (int i = threadIdx.x; i < nl * S; i += kThreads) mask[i] = 0;
     __syncthreads();
 
-    // 2. bit masks per (expert, sub-tile); offsets = exclusive scan of totals
+    // 2. bit masks per (expert, sub-tile); offsets = exclusive scan of the
+    //    padded segment lengths
     if (mine) {
 #pragma unroll
         for (int j = 0; j < KMAX; ++j)
@@ -208,12 +211,15 @@ __global__ __launch_bounds__(kThreads) void map_place_kernel(
         const int ex = e0 + i;
         if (ex >= nl) break;
         const int32_t tot = static_cast<int32_t>(before_sub[ex]);
+        const int32_t padded = (tot + align - 1) / align * align;
         if (tile == 0) {
             counts[ex] = tot;
             offsets[ex] = run;
+            if (row_src != nullptr)   // padding rows have no source token
+                for (int32_t r = run + tot; r < run + padded; ++r) row_src[r] = -1;
         }
         base[ex] += run;
-        run += tot;
+        run += padded;
     }
     if (tile == 0 && threadIdx.x == 0) offsets[nl] = grand;
     __syncthreads();
@@ -265,12 +271,14 @@ TK_EXPORT size_t tk_map_workspace_bytes(int32_t T, int32_t k, int32_t n_local)
     return (static_cast<size_t>(n_local) * g.pitch + static_cast<size_t>(n_local)) * sizeof(int32_t);
 }
 
-TK_EXPORT tk_status tk_map(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
-                           int32_t local_begin, int32_t local_end, int32_t* counts,
-                           int32_t* offsets, int32_t* pos, int32_t* row_src, void* workspace,
-                           size_t workspace_bytes, hipStream_t stream)
+TK_EXPORT tk_status tk_map_aligned(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
+                                   int32_t local_begin, int32_t local_end, int32_t align,
+                                   int32_t* counts, int32_t* offsets, int32_t* pos,
+                                   int32_t* row_src, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream)
 {
     using tk::fail;
+    if (align < 1) return fail(TK_ERR_ARG, "tk_map: align=%d < 1", align);
     if (T < 0) return fail(TK_ERR_ARG, "tk_map: T=%d < 0", T);
     if (k < 1) return fail(TK_ERR_ARG, "tk_map: k=%d < 1", k);
     if (k > TK_MAX_TOPK) return fail(TK_ERR_UNSUPPORTED, "tk_map: k=%d > %d", k, TK_MAX_TOPK);
@@ -280,8 +288,9 @@ TK_EXPORT tk_status tk_map(const int32_t* topk_idx, int32_t T, int32_t k, int32_
     if (local_begin < 0 || local_end > E || local_begin >= local_end)
         return fail(TK_ERR_ARG, "tk_map: local range [%d, %d) not a non-empty part of [0, %d)",
                     local_begin, local_end, E);
-    if (static_cast<int64_t>(T) * k > INT32_MAX)
-        return fail(TK_ERR_ARG, "tk_map: T*k exceeds int32 positions");
+    if (static_cast<int64_t>(T) * k +
+            static_cast<int64_t>(local_end - local_begin) * (align - 1) > INT32_MAX)
+        return fail(TK_ERR_ARG, "tk_map: T*k plus padding exceeds int32 positions");
     if (counts == nullptr || offsets == nullptr)
         return fail(TK_ERR_ARG, "tk_map: NULL counts/offsets");
     if (T > 0 && (topk_idx == nullptr || pos == nullptr))
@@ -320,10 +329,19 @@ TK_EXPORT tk_status tk_map(const int32_t* topk_idx, int32_t T, int32_t k, int32_
     const size_t lds = (2 * static_cast<size_t>(nl) * g.S + nl) * sizeof(uint32_t);
     e = small_k
         ? tk::launch(map_place_kernel<8>, grid, block, lds, stream, topk_idx, T, k, local_begin,
-                     local_end, g.S, g.n_tiles, g.pitch, g.fused ? 1 : 0, cnt, totals, counts,
-                     offsets, pos, row_src)
+                     local_end, g.S, g.n_tiles, g.pitch, g.fused ? 1 : 0, align, cnt, totals,
+                     counts, offsets, pos, row_src)
         : tk::launch(map_place_kernel<TK_MAX_TOPK>, grid, block, lds, stream, topk_idx, T, k,
-                     local_begin, local_end, g.S, g.n_tiles, g.pitch, g.fused ? 1 : 0, cnt, totals,
-                     counts, offsets, pos, row_src);
+                     local_begin, local_end, g.S, g.n_tiles, g.pitch, g.fused ? 1 : 0, align, cnt,
+                     totals, counts, offsets, pos, row_src);
     return tk::launched(e, "tk_map (place)");
+}
+
+TK_EXPORT tk_status tk_map(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
+                           int32_t local_begin, int32_t local_end, int32_t* counts,
+                           int32_t* offsets, int32_t* pos, int32_t* row_src, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream)
+{
+    return tk_map_aligned(topk_idx, T, k, E, local_begin, local_end, 1, counts, offsets, pos,
+                          row_src, workspace, workspace_bytes, stream);
 }

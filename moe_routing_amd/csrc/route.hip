@@ -17,38 +17,6 @@
 
 namespace {
 
-// Pinned fp32 e^y: Cody & Waite reduction by ln 2 split in two words (the
-// high word has 16 significant bits, so n*LN2_HI is exact for |n| <= 128),
-// then the degree-7 Taylor polynomial of e^r in Horner form with fused
-// multiply-adds.  Every step is one IEEE fp32 operation (the file is built
-// with -ffp-contract=off), so the result is the same on any IEEE machine
-// that follows these steps; y is cut to [-86, 88] so p * 2^n stays normal.
-constexpr float kLog2e = 0x1.715476p+0f;    // RN(log2 e)
-constexpr float kLn2Hi = 0x1.62e4p-1f;      // ln 2 truncated to 16 bits
-constexpr float kLn2Lo = 0x1.7f7d1cp-20f;   // RN(ln 2 - kLn2Hi)
-constexpr float kC2 = 0x1p-1f, kC3 = 0x1.555556p-3f, kC4 = 0x1.555556p-5f,
-                kC5 = 0x1.111112p-7f, kC6 = 0x1.6c16c2p-10f, kC7 = 0x1.a01a02p-13f;  // RN(1/i!)
-
-__device__ __forceinline__ float pinned_exp(float y)
-{
-    if (y > 88.0f) return __builtin_inff();
-    if (y < -86.0f) return 0.0f;
-    const float n = __builtin_rintf(y * kLog2e);
-    float r = __builtin_fmaf(-n, kLn2Hi, y);
-    r = __builtin_fmaf(-n, kLn2Lo, r);
-    float p = kC7;
-    p = __builtin_fmaf(p, r, kC6);
-    p = __builtin_fmaf(p, r, kC5);
-    p = __builtin_fmaf(p, r, kC4);
-    p = __builtin_fmaf(p, r, kC3);
-    p = __builtin_fmaf(p, r, kC2);
-    p = __builtin_fmaf(p, r, 1.0f);
-    p = __builtin_fmaf(p, r, 1.0f);
-    return __builtin_ldexpf(p, static_cast<int>(n));
-}
-
-__device__ __forceinline__ float pinned_sigmoid(float x) { return 1.0f / (1.0f + pinned_exp(-x)); }
-
 // Order-preserving map fp32 -> uint32 with -0 folded onto +0; every real key
 // (including -inf) maps above 0, which marks "not eligible".
 __device__ __forceinline__ uint32_t order_key(float f)
@@ -116,7 +84,7 @@ __global__ __launch_bounds__(tk::kBlock) void route_kernel(RouteArgs a)
         const int e = e0 + i;
         float kf;
         if (sigmoid) {
-            s[i] = pinned_sigmoid(x[i]);
+            s[i] = tk::pinned_sigmoid(x[i]);
             kf = (a.bias != nullptr && e < a.E) ? s[i] + a.bias[e] : s[i];
         } else {
             s[i] = x[i];
@@ -317,7 +285,7 @@ __global__ __launch_bounds__(tk::kBlock) void route_fast_kernel(FastArgs a)
     for (int i = 0; i < EPL; ++i) {
         float kf;
         if constexpr (SIGMOID) {
-            sc[i] = pinned_sigmoid(x[i]);
+            sc[i] = tk::pinned_sigmoid(x[i]);
             kf = has_bias ? sc[i] + b[i] : sc[i];
         } else {
             sc[i] = x[i];

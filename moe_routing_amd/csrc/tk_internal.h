@@ -130,4 +130,64 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
            (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
 }
 
+// ------------------------------------------------ shared fp32 arithmetic
+// Pinned fp32 e^y: Cody & Waite reduction by ln 2 split in two words (the
+// high word has 16 significant bits, so n*LN2_HI is exact for |n| <= 128),
+// then the degree-7 Taylor polynomial of e^r in Horner form with fused
+// multiply-adds.  Every step is one IEEE fp32 operation (the library is built
+// with -ffp-contract=off), so the result is the same on any IEEE machine
+// that follows these steps; y is cut to [-86, 88] so p * 2^n stays normal.
+constexpr float kLog2e = 0x1.715476p+0f;    // RN(log2 e)
+constexpr float kLn2Hi = 0x1.62e4p-1f;      // ln 2 truncated to 16 bits
+constexpr float kLn2Lo = 0x1.7f7d1cp-20f;   // RN(ln 2 - kLn2Hi)
+constexpr float kC2 = 0x1p-1f, kC3 = 0x1.555556p-3f, kC4 = 0x1.555556p-5f,
+                kC5 = 0x1.111112p-7f, kC6 = 0x1.6c16c2p-10f, kC7 = 0x1.a01a02p-13f;  // RN(1/i!)
+
+__device__ __forceinline__ float pinned_exp(float y)
+{
+    if (y > 88.0f) return __builtin_inff();
+    if (y < -86.0f) return 0.0f;
+    const float n = __builtin_rintf(y * kLog2e);
+    float r = __builtin_fmaf(-n, kLn2Hi, y);
+    r = __builtin_fmaf(-n, kLn2Lo, r);
+    float p = kC7;
+    p = __builtin_fmaf(p, r, kC6);
+    p = __builtin_fmaf(p, r, kC5);
+    p = __builtin_fmaf(p, r, kC4);
+    p = __builtin_fmaf(p, r, kC3);
+    p = __builtin_fmaf(p, r, kC2);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    return __builtin_ldexpf(p, static_cast<int>(n));
+}
+
+__device__ __forceinline__ float pinned_sigmoid(float x) { return 1.0f / (1.0f + pinned_exp(-x)); }
+
+// -------------------------------------------------- 1x128 E4M3 codec
+// x / scale for scale > 0 by Markstein's correction on the correctly rounded
+// reciprocal inv = RN(1/scale): q0 = RN(x*inv); r = fma(-q0, scale, x) (exact);
+// q = RN(q0 + r*inv) is the correctly rounded quotient (P. Markstein, IBM J.
+// Res. Dev. 34(1), 1990; Muller et al., Handbook of Floating-Point
+// Arithmetic).  Quotients that underflow encode to a signed E4M3 zero either
+// way.  The correction step maps x = -0 to +0 (the sum +0 + -0 rounds to +0),
+// so the sign of x is put back; for x != 0 the sign is already right and
+// copysign changes nothing.
+__device__ __forceinline__ float fp8_quotient(float x, float scale, float inv)
+{
+    const float q0 = x * inv;
+    const float r = __builtin_fmaf(-q0, scale, x);
+    return __builtin_copysignf(__builtin_fmaf(r, inv, q0), x);
+}
+
+// Four quotients -> four E4M3 codes (gfx950 hardware convert: OCP E4M3FN,
+// round to nearest even).  amax / RN(amax/448) can exceed 448 by one fp32
+// ulp; such values round to 448 like every value below 464.
+__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d)
+{
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return static_cast<uint32_t>(w);
+}
+
+
 }  // namespace tk

@@ -29,7 +29,8 @@ def lib():
         __graft_entry__.build()
     L = ctypes.CDLL(LIB)
     L.tk_last_error.restype = ctypes.c_char_p
-    for name in ("tk_route", "tk_map", "tk_expand_quant", "tk_reduce", "tk_expert_standin"):
+    for name in ("tk_route", "tk_map", "tk_map_aligned", "tk_expand_quant", "tk_reduce",
+                 "tk_expert_standin", "tk_swiglu_quant"):
         getattr(L, name).restype = ctypes.c_int32
     L.tk_map_workspace_bytes.restype = ctypes.c_size_t
     return L
@@ -37,7 +38,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["tk_last_error", "tk_route", "tk_map_workspace_bytes", "tk_map",
-                                  "tk_expand_quant", "tk_reduce", "tk_expert_standin"])
+                                  "tk_map_aligned", "tk_expand_quant", "tk_reduce",
+                                  "tk_expert_standin", "tk_swiglu_quant"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -172,3 +174,39 @@ def test_product_path_never_uses_the_oracle():
                 text = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert not re.search(r"import\s+oracle|from\s+oracle|liboracle|\borc_\w+",
                                      text), f
+
+
+def _swiglu(lib, cap, I, h=FAKE, n_rows=None, row_src=None, pos=None, w=None, T=0, k=0, out=FAKE,
+            scales=FAKE):
+    I32 = ctypes.c_int32
+    return lib.tk_swiglu_quant(h, ctypes.c_int64(cap), n_rows, I32(I), row_src, pos, w, I32(T),
+                               I32(k), out, scales, None)
+
+
+def test_swiglu_rejects_bad_arguments(lib):
+    assert _swiglu(lib, -1, 256) == ARG
+    assert _swiglu(lib, 8, 0) == ARG
+    assert _swiglu(lib, 8, 200) == ARG                       # I % 128 != 0
+    assert _swiglu(lib, 8, 256, row_src=FAKE) == ARG         # weights need all three
+    assert b"together" in lib.tk_last_error()
+    assert _swiglu(lib, 8, 256, row_src=FAKE, pos=FAKE, w=FAKE, T=4, k=0) == ARG
+    assert _swiglu(lib, 8, 256, row_src=FAKE, pos=FAKE, w=FAKE, T=4, k=33) == ARG
+    assert _swiglu(lib, 8, 256, h=None) == ARG
+    assert _swiglu(lib, 8, 256, out=MIS) == ARG
+    assert _swiglu(lib, 8, 256, scales=MIS1) == ARG
+    assert _swiglu(lib, 0, 256, h=None, out=None, scales=None) == 0   # nothing to do
+
+
+def test_map_aligned_rejects_bad_arguments(lib):
+    I = ctypes.c_int32
+    ws = ctypes.c_size_t(1 << 20)
+
+    def call(T, k, E, lo, hi, align):
+        return lib.tk_map_aligned(FAKE, I(T), I(k), I(E), I(lo), I(hi), I(align), FAKE, FAKE,
+                                  FAKE, None, FAKE, ws, None)
+
+    assert call(4, 8, 256, 0, 256, 0) == ARG
+    assert call(4, 8, 256, 0, 256, -3) == ARG
+    # T*k plus the largest padding must fit in int32 positions
+    assert call(1 << 27, 8, 256, 0, 256, 1 << 24) == ARG
+    assert b"padding" in lib.tk_last_error()

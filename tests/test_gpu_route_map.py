@@ -171,3 +171,57 @@ def test_map_deterministic():
     b = [to_host(t) for t in tk.tk_map(idx, 256)]
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+# ------------------------------------------------------------- aligned map --
+@pytest.mark.parametrize("T,E,k,lo,hi,align", [
+    (1, 8, 1, 0, 8, 128), (300, 16, 2, 0, 16, 1), (1000, 256, 8, 32, 64, 128),
+    (4097, 256, 8, 0, 256, 128), (777, 64, 3, 0, 64, 7), (2049, 32, 4, 7, 8, 1000),
+    (70000, 256, 8, 0, 256, 64), (300, 1024, 32, 0, 1024, 16),
+])
+def test_map_aligned_random_routing(T, E, k, lo, hi, align):
+    rng = np.random.default_rng(T + E + align)
+    idx = synth.random_routing(rng, T, E, k)
+    g = [to_host(t) for t in tk.tk_map_aligned(to_dev(idx), E, lo, hi, align)]
+    torch.cuda.synchronize()
+    oc, oo, op, ors = oracle.map_aligned(idx, E, lo, hi, align)
+    assert np.array_equal(g[0], oc), "counts"
+    assert np.array_equal(g[1], oo), "offsets"
+    assert np.array_equal(g[2], op), "pos"
+    assert np.array_equal(g[3][: int(oo[-1])], ors), "row_src (with -1 on padding rows)"
+
+
+def test_map_aligned_v3_full():
+    cfg = synth.v3_gate(0)
+    idx, _ = oracle.route(cfg["logits"], cfg["bias"], cfg["k"], **cfg["route"])
+    g = [to_host(t) for t in tk.tk_map_aligned(to_dev(idx), 256, 0, 256, 128)]
+    oc, oo, op, ors = oracle.map_aligned(idx, 256, 0, 256, 128)
+    assert np.array_equal(g[0], oc) and np.array_equal(g[1], oo) and np.array_equal(g[2], op)
+    assert np.array_equal(g[3][: int(oo[-1])], ors)
+    assert np.all(oo % 128 == 0)
+
+
+def test_aligned_layout_gives_the_same_rows_and_combine():
+    """Expanded rows and the combine do not depend on the layout: with y rows
+    moved to the aligned positions, the reduce output is bitwise the same."""
+    rng = np.random.default_rng(90)
+    T, E, k, H, align = 700, 32, 4, 1024, 128
+    idx = synth.random_routing(rng, T, E, k)
+    x = synth.normal_bf16(rng, (T, H))
+    w = rng.random((T, k)).astype(np.float32)
+    idx_d, x_d, w_d = to_dev(idx), to_dev(x, bf16=True), to_dev(w)
+    _, off_p, pos_p, _ = tk.tk_map(idx_d, E)
+    _, off_a, pos_a, _ = tk.tk_map_aligned(idx_d, E, 0, E, align)
+    R, cap = T * k, T * k + E * (align - 1)
+    assert int(off_a[-1]) <= cap
+    xq_p, sc_p = tk.tk_expand_quant(x_d, pos_p, tk.TK_EXPAND_FP8_E4M3_1X128, R)
+    xq_a, sc_a = tk.tk_expand_quant(x_d, pos_a, tk.TK_EXPAND_FP8_E4M3_1X128, cap)
+    pp, pa = pos_p.view(-1).long(), pos_a.view(-1).long()
+    assert torch.equal(xq_a[pa], xq_p[pp]) and torch.equal(sc_a[pa], sc_p[pp])
+    y_p = to_dev(synth.normal_bf16(rng, (R, H)), bf16=True)
+    y_a = torch.zeros((cap, H), dtype=torch.bfloat16, device="cuda")
+    y_a[pa] = y_p[pp]
+    out_p = tk.tk_reduce(y_p, pos_p, w_d)
+    out_a = tk.tk_reduce(y_a, pos_a, w_d)
+    torch.cuda.synchronize()
+    assert torch.equal(out_p.view(torch.int16), out_a.view(torch.int16))

@@ -1,0 +1,123 @@
+"""GPU parity of tk_swiglu_quant (SwiGLU + 1x128 FP8 quantisation, optionally
+weighted by each row's routing weight) against the CPU oracle.
+
+FP8 codes and scales: bit-exact.  Shapes span one block, ragged chunk tails
+(I not a multiple of 1024), a device-side row count below the capacity, the
+weighted form driven by a real map, codec corners of the activation, and the
+DeepSeek-V3 expert shape (65536 rows, I = 2048) checked on sampled rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from moe_routing_amd import synth
+from tk_testutil import to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+tk = pytest.importorskip("moe_routing_amd")
+
+
+def _rows(rng, R, I, gscale=2.0):
+    g = synth.normal_f32(rng, (R, I)) * np.float32(gscale)
+    u = synth.normal_f32(rng, (R, I))
+    return synth.bf16_bits(np.concatenate([g, u], axis=1))
+
+
+def _map(rng, T, E, k, lo, hi):
+    idx = synth.random_routing(rng, T, E, k)
+    _, offsets, pos, row_src = oracle.map_routes(idx, E, lo, hi)
+    w = rng.uniform(0.01, 1.0, (T, k)).astype(np.float32)
+    return pos, row_src, w, int(offsets[-1])
+
+
+def _check(h, I, got_q, got_s, rows, row_w=None):
+    q_ref, s_ref = oracle.swiglu_quant(h[:rows], I, None if row_w is None else row_w[:rows])
+    g_q, g_s = got_q[:rows], got_s[:rows]
+    bad = np.nonzero((g_q != q_ref).any(1) | (g_s != s_ref).any(1))[0]
+    assert bad.size == 0, f"{bad.size} rows differ, first {bad[:5]}"
+
+
+@pytest.mark.parametrize("R,I", [(64, 128), (100, 384), (257, 1152), (512, 2048), (33, 7168)])
+def test_swiglu_quant_random(R, I):
+    rng = np.random.default_rng(R + I)
+    h = _rows(rng, R, I)
+    q, s = tk.tk_swiglu_quant(to_dev(h, bf16=True))
+    torch.cuda.synchronize()
+    _check(h, I, to_host(q), to_host(s), R)
+
+
+@pytest.mark.parametrize("T,E,k,lo,hi,I", [(300, 32, 4, 0, 32, 256), (500, 64, 8, 16, 48, 1152),
+                                          (129, 16, 2, 0, 16, 2048)])
+def test_swiglu_quant_weighted_by_map(T, E, k, lo, hi, I):
+    rng = np.random.default_rng(T + E + I)
+    pos, row_src, w, R = _map(rng, T, E, k, lo, hi)
+    cap = R + 5
+    h = _rows(rng, cap, I)
+    n_rows = torch.tensor([R], dtype=torch.int32, device="cuda")
+    rs = np.full(cap, -1, np.int32)
+    rs[:R] = row_src
+    out = torch.full((cap, I), 0x33, dtype=torch.uint8, device="cuda")
+    sc = torch.full((cap, I // 128), -2.0, dtype=torch.float32, device="cuda")
+    tk.tk_swiglu_quant(to_dev(h, bf16=True), n_rows, to_dev(rs), to_dev(pos), to_dev(w), out, sc)
+    torch.cuda.synchronize()
+    g_q, g_s = to_host(out), to_host(sc)
+    _check(h, I, g_q, g_s, R, oracle.row_weights(pos, w, R))
+    assert np.all(g_q[R:] == 0x33) and np.all(g_s[R:] == -2.0), "wrote rows at or beyond n_rows"
+
+
+def test_swiglu_quant_corners():
+    rng = np.random.default_rng(80)
+    I = 1024
+    # (activations that overflow fp32 are outside the contract: gates stay
+    # small enough that g * u is finite)
+    specials = np.array([0.0, -0.0, 20.0, -20.0, 100.0, -100.0, 88.5, -88.5, 1e-30, -3e-5,
+                         1.0e30, -65504.0, 0.5, -1.0], np.float32)
+    R = 40
+    g = rng.choice(specials, (R, I)).astype(np.float32)
+    g[::3] = synth.normal_f32(rng, (len(g[::3]), I)) * np.float32(8.0)
+    u = synth.normal_f32(rng, (R, I))
+    u[1::4] = 0.0
+    u[2::4] *= np.float32(1e-20)
+    u[3] = rng.choice(specials[:10], I)
+    h = synth.bf16_bits(np.concatenate([g, u], axis=1))
+    q, s = tk.tk_swiglu_quant(to_dev(h, bf16=True))
+    torch.cuda.synchronize()
+    _check(h, I, to_host(q), to_host(s), R)
+
+
+def test_swiglu_quant_zero_rows_and_deterministic():
+    rng = np.random.default_rng(81)
+    h = to_dev(_rows(rng, 300, 512), bf16=True)
+    n0 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = torch.full((300, 512), 7, dtype=torch.uint8, device="cuda")
+    sc = torch.zeros((300, 4), dtype=torch.float32, device="cuda")
+    tk.tk_swiglu_quant(h, n0, out=out, scales=sc)
+    torch.cuda.synchronize()
+    assert np.all(to_host(out) == 7)
+    a = [to_host(t) for t in tk.tk_swiglu_quant(h)]
+    b = [to_host(t) for t in tk.tk_swiglu_quant(h)]
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+
+
+def test_swiglu_quant_v3_expert_shape_sampled():
+    """65536 expanded rows of the DeepSeek-V3 routing, I = 2048, weighted by the
+    routing weights through the map; 512 sampled rows against the oracle."""
+    cfg = synth.v3_gate(0)
+    idx, w = oracle.route(cfg["logits"], cfg["bias"], cfg["k"], **cfg["route"])
+    w = w.astype(np.float32)
+    _, offsets, pos, row_src = oracle.map_routes(idx, 256)
+    R, I = int(offsets[-1]), 2048
+    h = synth.normal_bf16(np.random.default_rng(7), (R, 2 * I))
+    h_d = to_dev(h, bf16=True)
+    q, s = tk.tk_swiglu_quant(h_d, None, to_dev(row_src), to_dev(pos), to_dev(w))
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(82).choice(R, 512, replace=False))
+    rows = np.concatenate([[0], rows, [R - 1]])
+    ridx = torch.from_numpy(rows).to("cuda")
+    h_s = h[rows]
+    rw = oracle.row_weights(pos, w, R)[rows]
+    q_ref, s_ref = oracle.swiglu_quant(h_s, I, rw)
+    assert np.array_equal(to_host(q.index_select(0, ridx)), q_ref)
+    assert np.array_equal(to_host(s.index_select(0, ridx)), s_ref)
