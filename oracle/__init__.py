@@ -56,6 +56,8 @@ def _declare(L: ctypes.CDLL) -> ctypes.CDLL:
     L.orc_map.restype = i32
     L.orc_map_aligned.argtypes = [vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]
     L.orc_map_aligned.restype = i32
+    L.orc_balance_loss.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp]
+    L.orc_balance_loss.restype = i32
     L.orc_expand.argtypes = [vp, i32, i32, i32, vp, i32, i64, vp, vp]
     L.orc_expand.restype = i32
     L.orc_quant_row.argtypes = [vp, i32, vp, vp]
@@ -177,6 +179,21 @@ def map_routes(topk_idx, E: int, lo: int = 0, hi: int | None = None, with_row_sr
     if with_row_src:
         row_src = row_src[: int(offsets[-1])].copy()
     return counts, offsets, pos, row_src
+
+
+def balance_loss(logits, topk_idx, score: int):
+    """(f, P, loss): per-expert load fraction E/(kT)*count, mean normalised
+    score, and sum_e f_e P_e (fp64)."""
+    logits = _c(logits, np.float32)
+    topk_idx = _c(topk_idx, np.int32)
+    T, E = logits.shape
+    k = topk_idx.shape[1]
+    f = np.empty(E, np.float64)
+    P = np.empty(E, np.float64)
+    loss = np.empty(1, np.float64)
+    if lib().orc_balance_loss(_p(logits), T, E, k, score, _p(topk_idx), _p(f), _p(P), _p(loss)) != 0:
+        raise ValueError("oracle balance_loss: unsupported arguments")
+    return f, P, float(loss[0])
 
 
 def map_aligned(topk_idx, E: int, lo: int = 0, hi: int | None = None, align: int = 1):

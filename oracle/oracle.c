@@ -299,6 +299,54 @@ int orc_route(const float* logits, const float* bias, int T, int E, int k,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Load-balance statistics and loss over one batch of T tokens (the          */
+/* "load-balancing loss computation" of TileKernels' moe/ module), in the    */
+/* form DeepSeek-V3 trains with:                                             */
+/*   count_e = number of routes (t, j) with topk_idx[t,j] = e                 */
+/*   f_e     = E / (k T) * count_e            (1 for a perfectly even load)   */
+/*   p_{t,e} = normalised score of e for token t: sigmoid scores divided by    */
+/*             their sum over all E experts, or the softmax probabilities     */
+/*   P_e     = (1/T) sum_t p_{t,e}                                            */
+/*   loss    = sum_e f_e P_e                   (the caller applies its weight)*/
+/* Sigmoid scores are the pinned fp32 orc_sigmoid_f32 (the same scores the   */
+/* route ranks on); everything after them is fp64.  Softmax is fp64.         */
+/* ------------------------------------------------------------------------ */
+int orc_balance_loss(const float* logits, int T, int E, int k, int score,
+                     const int32_t* topk_idx, double* f, double* P, double* loss)
+{
+    if (T < 1 || E < 1 || k < 1) return -1;
+    double* p = (double*)malloc(sizeof(double) * (size_t)E);
+    int64_t* count = (int64_t*)calloc((size_t)E, sizeof(int64_t));
+    if (!p || !count) { free(p); free(count); return -1; }
+    for (int e = 0; e < E; ++e) P[e] = 0.0;
+    for (int t = 0; t < T; ++t) {
+        const float* x = logits + (size_t)t * E;
+        double z = 0.0;
+        if (score == ORC_SIGMOID) {
+            for (int e = 0; e < E; ++e) { p[e] = (double)orc_sigmoid_f32(x[e]); z += p[e]; }
+        } else {
+            double m = (double)x[0];
+            for (int e = 1; e < E; ++e) if ((double)x[e] > m) m = (double)x[e];
+            for (int e = 0; e < E; ++e) { p[e] = exp((double)x[e] - m); z += p[e]; }
+        }
+        for (int e = 0; e < E; ++e) P[e] += p[e] / z;
+        for (int j = 0; j < k; ++j) {
+            const int32_t e = topk_idx[(size_t)t * k + j];
+            if (e >= 0 && e < E) count[e] += 1;
+        }
+    }
+    double l = 0.0;
+    for (int e = 0; e < E; ++e) {
+        P[e] /= (double)T;
+        f[e] = (double)E / ((double)k * (double)T) * (double)count[e];
+        l += f[e] * P[e];
+    }
+    *loss = l;
+    free(p); free(count);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Map: local mask, per-expert counts, exclusive offsets, stable positions.  */
 /*                                                                           */
 /* A route (t, j) is local when lo <= topk_idx[t,j] < hi (the mask of the    */
