@@ -155,6 +155,69 @@ def bench_swiglu(tk, torch, y, n_rows, row_src, pos, w, steps):
                          "ops_per_element": SWIGLU_OPS_PER_ELEM}}
 
 
+def _time_calls(torch, call, steps, outputs):
+    """GPU time per call of a short, launch-bound call: `steps` calls are
+    captured in one HIP graph and the graph is replayed, so the host-side cost
+    of the Python binding does not leave the GPU idle between calls.  The
+    graph's outputs are checked against an eager call first."""
+    call()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in outputs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):          # warm-up on a side stream before capture
+        for _ in range(2):
+            call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(steps):
+            call()
+    g.replay()
+    torch.cuda.synchronize()
+    if not all(torch.equal(a, b) for a, b in zip(eager, outputs)):
+        raise RuntimeError("graph replay differs from the eager call")
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / steps
+
+
+def bench_map_balance(tk, torch, logits, idx, steps):
+    """The map with expert segments padded to 128 rows (grouped-GEMM layout),
+    and the load-balance statistics + loss, on the step's routing."""
+    dev = logits.device
+    align = 128
+    cap = T * K + E * (align - 1)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    pos = torch.empty((T, K), dtype=torch.int32, device=dev)
+    row_src = torch.empty(cap, dtype=torch.int32, device=dev)
+    ws = torch.empty(max(tk.tk_map_workspace_bytes(T, K, E), 16), dtype=torch.uint8, device=dev)
+    us_map = _time_calls(torch, lambda: tk.tk_map_aligned(idx, E, 0, E, align, counts, offsets,
+                                                          pos, row_src, ws), steps,
+                         (counts, offsets, pos))
+    f = torch.empty(E, dtype=torch.float32, device=dev)
+    P = torch.empty(E, dtype=torch.float32, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    wsb = torch.empty(max(tk.library().tk_balance_workspace_bytes(T, E), 16), dtype=torch.uint8,
+                      device=dev)
+    us_bal = _time_calls(torch, lambda: tk.tk_balance_loss(logits, idx, tk.TK_SCORE_SIGMOID, f, P,
+                                                           loss, wsb), steps, (f, P, loss))
+    bal_bytes = T * E * 4 + T * K * 4 + 2 * E * 4 + 4
+    return {"map_aligned_128": {"workload": f"T={T}, k={K}, E={E}, segments padded to {align} rows",
+                                "us_per_call": round(us_map, 2), "timing": "HIP graph of the calls",
+                                "bound": "latency (two dependent launches)"},
+            "balance_loss": {"workload": f"T={T}, E={E}, k={K}, sigmoid scores",
+                             "us_per_call": round(us_bal, 2), "timing": "HIP graph of the calls",
+                             "hbm_gbps": round(bal_bytes / us_bal / 1e3, 1),
+                             "bound": "latency (two dependent launches)"}}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -265,7 +328,8 @@ def main() -> int:
         torch.cuda.synchronize()
 
     next_rows = {"swiglu_quant_fp8": bench_swiglu(tk, torch, y, offsets[E:], row_src, pos, w,
-                                                  args.steps)}
+                                                  args.steps),
+                 **bench_map_balance(tk, torch, logits, idx, args.steps)}
 
     ms_per_step = total_ms / args.steps
     value = T / (ms_per_step * 1e-3)

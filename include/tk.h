@@ -10,6 +10,11 @@
  *                    optionally fused 1x128 FP8 E4M3 quant    scales])
  *   tk_reduce        weighted combine back to tokens        (rows, w -> out)
  *
+ * per-expert load statistics and the load-balance loss,
+ *
+ *   tk_balance_loss  f, P and sum_e f_e P_e of one batch    (logits, idx ->
+ *                                                             f, P, loss)
+ *
  * the next step after an expert's first grouped GEMM,
  *
  *   tk_swiglu_quant  SwiGLU + 1x128 FP8 quantisation        (rows -> codes,
@@ -234,6 +239,35 @@ tk_status tk_expand_quant(const void* x_bf16, int32_t T, int32_t H, int32_t k,
  */
 tk_status tk_reduce(const void* y_bf16, int64_t rows, const int32_t* pos, const float* topk_w,
                     int32_t T, int32_t k, int32_t H, void* out_bf16, hipStream_t stream);
+
+/* ------------------------------------------------------ load balance */
+/* Bytes of device workspace tk_balance_loss needs for T tokens and E experts. */
+size_t tk_balance_workspace_bytes(int32_t T, int32_t E);
+
+/*
+ * tk_balance_loss -- per-expert load statistics and the load-balance loss of
+ * one batch: the "load-balancing loss computation" of TileKernels' moe/
+ * module ("刚刚！DeepSeek开源高性能GPU算子库TileKernels", item moe/), in the form
+ * DeepSeek-V3 trains with:
+ *   count_e = number of (t, j) with topk_idx[t,j] = e (ids outside [0,E) ignored)
+ *   f[e]    = E / (k*T) * count_e             (1 everywhere for an even load)
+ *   P[e]    = (1/T) sum_t p_{t,e}, with p_{t,.} the token's scores over all E
+ *             experts normalised to sum 1: sigmoid scores (the pinned sigmoid
+ *             of tk_route, no bias) divided by their sum, or the softmax
+ *   loss[0] = sum_e f[e] * P[e]               (the caller applies its weight)
+ * fp32 sums in a fixed order (deterministic); the loss is accumulated in fp64.
+ *
+ * logits     device, fp32 (T, E), the router logits tk_route ranked
+ * topk_idx   device, int32 (T, k), the experts tk_route chose
+ * T, E, k    T >= 1; 1 <= E <= TK_MAX_EXPERTS; 1 <= k <= TK_MAX_TOPK
+ * score      TK_SCORE_SIGMOID or TK_SCORE_SOFTMAX
+ * f, P       device, fp32 (E) out;  loss: device, fp32 (1) out
+ * workspace  device, >= tk_balance_workspace_bytes(T, E) bytes, 4-byte aligned;
+ *            scratch, contents on entry ignored
+ */
+tk_status tk_balance_loss(const float* logits, const int32_t* topk_idx, int32_t T, int32_t E,
+                          int32_t k, int32_t score, float* f, float* P, float* loss,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------- SwiGLU + FP8 quant */
 /*

@@ -13,6 +13,7 @@ step of the path runs in the library's HIP kernels; there is no fallback.
     tk_reduce(y, pos, topk_w)                  -> out
     tk_expert_standin(xq, scales, n_rows, mult) -> y
     tk_swiglu_quant(h, I, n_rows, row_src, pos, topk_w) -> (out, scales)
+    tk_balance_loss(logits, topk_idx, score)   -> (f, P, loss)
 """
 from __future__ import annotations
 
@@ -90,6 +91,10 @@ def library() -> ctypes.CDLL:
         L.tk_expert_standin.restype = i32
         L.tk_swiglu_quant.argtypes = [vp, i64, vp, i32, vp, vp, vp, i32, i32, vp, vp, vp]
         L.tk_swiglu_quant.restype = i32
+        L.tk_balance_workspace_bytes.argtypes = [i32, i32]
+        L.tk_balance_workspace_bytes.restype = sz
+        L.tk_balance_loss.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.tk_balance_loss.restype = i32
         _lib = L
     return _lib
 
@@ -270,3 +275,27 @@ def tk_swiglu_quant(h: torch.Tensor, n_rows: torch.Tensor | None = None,
         _ptr(h), cap, _ptr(n_rows), I, _ptr(row_src), _ptr(pos), _ptr(topk_w), T, k,
         _ptr(out), _ptr(scales), _stream(h)))
     return out, scales
+
+
+def tk_balance_loss(logits: torch.Tensor, topk_idx: torch.Tensor, score: int,
+                    f: torch.Tensor | None = None, P: torch.Tensor | None = None,
+                    loss: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Per-expert load fraction f, mean normalised score P and loss = sum f*P."""
+    _dev(logits, "logits", torch.float32, 2)
+    _dev(topk_idx, "topk_idx", torch.int32, 2)
+    T, E = logits.shape
+    k = topk_idx.shape[1]
+    dev = logits.device
+    f = torch.empty(E, dtype=torch.float32, device=dev) if f is None else f
+    P = torch.empty(E, dtype=torch.float32, device=dev) if P is None else P
+    loss = torch.empty(1, dtype=torch.float32, device=dev) if loss is None else loss
+    need = int(library().tk_balance_workspace_bytes(T, E))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    for name, t in (("f", f), ("P", P), ("loss", loss)):
+        _dev(t, name, torch.float32)
+    _dev(workspace, "workspace", torch.uint8)
+    _check("tk_balance_loss", library().tk_balance_loss(
+        _ptr(logits), _ptr(topk_idx), T, E, k, score, _ptr(f), _ptr(P), _ptr(loss),
+        _ptr(workspace), workspace.numel(), _stream(logits)))
+    return f, P, loss

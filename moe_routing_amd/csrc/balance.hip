@@ -1,0 +1,204 @@
+// tk_balance_loss: per-expert load statistics and the load-balance loss of
+// one batch -- the "load-balancing loss computation" of TileKernels' moe/
+// module ("刚刚！DeepSeek开源高性能GPU算子库TileKernels", item moe/), in the form
+// DeepSeek-V3 trains with:
+//   count_e = routes (t, j) with topk_idx[t,j] = e;  f_e = E/(k*T) * count_e
+//   P_e     = (1/T) sum_t p_{t,e}, p = sigmoid scores / their sum over all E
+//             experts (the pinned sigmoid of tk_route), or softmax probabilities
+//   loss    = sum_e f_e * P_e
+//
+// Two launches, every sum in a fixed order (deterministic):
+//   1. partial  one workgroup of 8 waves per tile of 32 tokens, one wave per
+//               token at a time (lane l holds experts [l*EPL, l*EPL+EPL), as
+//               in tk_route): the token's scores, their wave-wide sum (DPP
+//               row steps, then the rows in order), p;
+//               each wave accumulates p over its tokens in token order, the
+//               workgroup adds its waves in wave order -> part_p[tile][e];
+//               LDS integer histogram of the tile's routes -> part_c[tile][e]
+//   2. final    one workgroup: per expert, the tiles in order (four threads
+//               per expert over quarters of the tiles, added in quarter
+//               order), then f, P, and the loss accumulated in fp64.
+#include "tk_internal.h"
+
+namespace {
+
+constexpr int kTileTokens = 32;      // tokens per partial workgroup (4 per wave)
+constexpr int kPartialWaves = 8;
+constexpr int kPartialThreads = kPartialWaves * 64;
+constexpr int kFinalThreads = 1024;
+constexpr int kParts = 4;            // threads per expert in the final pass
+
+template <int EPL, bool SIGMOID>
+__global__ __launch_bounds__(kPartialThreads) void balance_partial_kernel(
+    const float* __restrict__ logits, const int32_t* __restrict__ idx, int T, int E, int k,
+    float* __restrict__ part_p, int32_t* __restrict__ part_c)
+{
+    __shared__ float wave_acc[kPartialWaves][tk::kWave * EPL];
+    extern __shared__ int32_t hist[];
+    const int lane = threadIdx.x & (tk::kWave - 1);
+    const int wave = tk::uniform(threadIdx.x / tk::kWave);
+    const int tile = blockIdx.x;
+    const int t0 = tile * kTileTokens;
+    for (int e = threadIdx.x; e < E; e += kPartialThreads) hist[e] = 0;
+    __syncthreads();
+    // routes of the tile
+    for (int i = threadIdx.x; i < kTileTokens * k; i += kPartialThreads) {
+        const int t = t0 + i / k;
+        if (t < T) {
+            const int32_t e = idx[static_cast<size_t>(t0) * k + i];
+            if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+        }
+    }
+    // normalised scores, accumulated in token order by each wave
+    float acc[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) acc[i] = 0.f;
+    const int e0 = lane * EPL;
+    for (int tt = wave; tt < kTileTokens; tt += kPartialWaves) {
+        const int t = t0 + tt;
+        if (t >= T) break;
+        const float* row = logits + static_cast<size_t>(t) * E;
+        float s[EPL];
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) s[i] = (e0 + i < E) ? row[e0 + i] : 0.f;
+        float m = 0.f;
+        if constexpr (!SIGMOID) {
+            m = -__builtin_inff();
+#pragma unroll
+            for (int i = 0; i < EPL; ++i)
+                if (e0 + i < E) m = fmaxf(m, s[i]);
+            m = tk::max_wave_f32(m);
+        }
+        float z = 0.f;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            if (e0 + i < E) s[i] = SIGMOID ? tk::pinned_sigmoid(s[i]) : expf(s[i] - m);
+            else s[i] = 0.f;
+            z += s[i];
+        }
+        z = tk::sum_wave_f32(z);
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) acc[i] += s[i] / z;
+    }
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) wave_acc[wave][e0 + i] = acc[i];
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += kPartialThreads) {
+        float v = wave_acc[0][e];
+#pragma unroll
+        for (int w = 1; w < kPartialWaves; ++w) v += wave_acc[w][e];
+        part_p[static_cast<size_t>(tile) * E + e] = v;
+        part_c[static_cast<size_t>(tile) * E + e] = hist[e];
+    }
+}
+
+__global__ __launch_bounds__(kFinalThreads) void balance_final_kernel(
+    const float* __restrict__ part_p, const int32_t* __restrict__ part_c, int n_tiles, int T,
+    int E, int k, float* __restrict__ f, float* __restrict__ P, float* __restrict__ loss)
+{
+    __shared__ float sp[kParts][TK_MAX_EXPERTS / kParts * kParts];
+    __shared__ int32_t sc[kParts][TK_MAX_EXPERTS / kParts * kParts];
+    __shared__ double red[kFinalThreads];
+    // thread (part, e) sums tiles [part*n/4, (part+1)*n/4) of expert e, in order
+    const int per = (n_tiles + kParts - 1) / kParts;
+    for (int i = threadIdx.x; i < kParts * E; i += kFinalThreads) {
+        const int part = i / E, e = i - part * E;
+        float v = 0.f;
+        int32_t c = 0;
+        const int a = part * per, b = min(n_tiles, a + per);
+        for (int tl = a; tl < b; ++tl) {
+            v += part_p[static_cast<size_t>(tl) * E + e];
+            c += part_c[static_cast<size_t>(tl) * E + e];
+        }
+        sp[part][e] = v;
+        sc[part][e] = c;
+    }
+    __syncthreads();
+    const double scale = static_cast<double>(E) / (static_cast<double>(k) * static_cast<double>(T));
+    double my = 0.0;
+    for (int e = threadIdx.x; e < E; e += kFinalThreads) {
+        float v = sp[0][e];
+        int64_t c = sc[0][e];
+#pragma unroll
+        for (int part = 1; part < kParts; ++part) {
+            v += sp[part][e];
+            c += sc[part][e];
+        }
+        const float pe = v / static_cast<float>(T);
+        const float fe = static_cast<float>(scale * static_cast<double>(c));
+        P[e] = pe;
+        f[e] = fe;
+        my += static_cast<double>(fe) * static_cast<double>(pe);
+    }
+    red[threadIdx.x] = my;
+    __syncthreads();
+    for (int w = kFinalThreads / 2; w > 0; w >>= 1) {
+        if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) loss[0] = static_cast<float>(red[0]);
+}
+
+int experts_per_lane(int E)
+{
+    int epl = 1;
+    while (epl * tk::kWave < E) epl *= 2;
+    return epl;
+}
+
+}  // namespace
+
+TK_EXPORT size_t tk_balance_workspace_bytes(int32_t T, int32_t E)
+{
+    if (T <= 0 || E <= 0) return 0;
+    const size_t n_tiles = (static_cast<size_t>(T) + kTileTokens - 1) / kTileTokens;
+    return n_tiles * static_cast<size_t>(E) * (sizeof(float) + sizeof(int32_t));
+}
+
+TK_EXPORT tk_status tk_balance_loss(const float* logits, const int32_t* topk_idx, int32_t T,
+                                    int32_t E, int32_t k, int32_t score, float* f, float* P,
+                                    float* loss, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream)
+{
+    using tk::fail;
+    if (T < 1) return fail(TK_ERR_ARG, "tk_balance_loss: T=%d < 1", T);
+    if (E < 1) return fail(TK_ERR_ARG, "tk_balance_loss: E=%d < 1", E);
+    if (E > TK_MAX_EXPERTS)
+        return fail(TK_ERR_UNSUPPORTED, "tk_balance_loss: E=%d > %d", E, TK_MAX_EXPERTS);
+    if (k < 1 || k > TK_MAX_TOPK) return fail(TK_ERR_ARG, "tk_balance_loss: k=%d invalid", k);
+    if (score != TK_SCORE_SOFTMAX && score != TK_SCORE_SIGMOID)
+        return fail(TK_ERR_ARG, "tk_balance_loss: unknown score %d", score);
+    if (logits == nullptr || topk_idx == nullptr || f == nullptr || P == nullptr || loss == nullptr)
+        return fail(TK_ERR_ARG, "tk_balance_loss: NULL pointer");
+    const size_t need = tk_balance_workspace_bytes(T, E);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(TK_ERR_ARG, "tk_balance_loss: workspace of %zu bytes < %zu needed",
+                    workspace_bytes, need);
+    if (!tk::aligned4(logits) || !tk::aligned4(topk_idx) || !tk::aligned4(f) ||
+        !tk::aligned4(P) || !tk::aligned4(loss) || !tk::aligned4(workspace))
+        return fail(TK_ERR_ARG, "tk_balance_loss: tensors must be 4-byte aligned");
+    const int n_tiles = (T + kTileTokens - 1) / kTileTokens;
+    float* part_p = static_cast<float*>(workspace);
+    int32_t* part_c = reinterpret_cast<int32_t*>(part_p + static_cast<size_t>(n_tiles) * E);
+    const dim3 grid(n_tiles), block(kPartialThreads);
+    const size_t lds = static_cast<size_t>(E) * sizeof(int32_t);
+    const bool sig = score == TK_SCORE_SIGMOID;
+    hipError_t e;
+#define TK_BALANCE(EPL_)                                                                           \
+    e = sig ? tk::launch(balance_partial_kernel<EPL_, true>, grid, block, lds, stream, logits,     \
+                         topk_idx, T, E, k, part_p, part_c)                                        \
+            : tk::launch(balance_partial_kernel<EPL_, false>, grid, block, lds, stream, logits,    \
+                         topk_idx, T, E, k, part_p, part_c)
+    switch (experts_per_lane(E)) {
+    case 1: TK_BALANCE(1); break;
+    case 2: TK_BALANCE(2); break;
+    case 4: TK_BALANCE(4); break;
+    case 8: TK_BALANCE(8); break;
+    default: TK_BALANCE(16); break;
+    }
+#undef TK_BALANCE
+    if (e != hipSuccess) return tk::launched(e, "tk_balance_loss (partial)");
+    e = tk::launch(balance_final_kernel, dim3(1), dim3(kFinalThreads), 0, stream, part_p, part_c,
+                   n_tiles, T, E, k, f, P, loss);
+    return tk::launched(e, "tk_balance_loss (final)");
+}

@@ -121,6 +121,35 @@ __device__ __forceinline__ uint32_t max_wave_u32(uint32_t v)
     return max(max(r0, r1), max(r2, r3));
 }
 
+// Sum / maximum over the whole wave, returned wave-uniform.  DPP row steps
+// then the four row results in a fixed order: every lane of a row holds the
+// same partial after each step (the pairs add in either order to the same
+// value), so the result does not depend on the lane and is deterministic.
+__device__ __forceinline__ float sum_wave_f32(float v)
+{
+    v += dpp_f32<kQuadXor1>(v);
+    v += dpp_f32<kQuadXor2>(v);
+    v += dpp_f32<kHalfMirror>(v);
+    v += dpp_f32<kMirror>(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 15));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 47));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+    return (r0 + r1) + (r2 + r3);
+}
+__device__ __forceinline__ float max_wave_f32(float v)
+{
+    v = fmaxf(v, dpp_f32<kQuadXor1>(v));
+    v = fmaxf(v, dpp_f32<kQuadXor2>(v));
+    v = fmaxf(v, dpp_f32<kHalfMirror>(v));
+    v = fmaxf(v, dpp_f32<kMirror>(v));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 15));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 47));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
 // Two fp32 -> two bf16 (round to nearest even, hardware convert) packed.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {

@@ -30,16 +30,18 @@ def lib():
     L = ctypes.CDLL(LIB)
     L.tk_last_error.restype = ctypes.c_char_p
     for name in ("tk_route", "tk_map", "tk_map_aligned", "tk_expand_quant", "tk_reduce",
-                 "tk_expert_standin", "tk_swiglu_quant"):
+                 "tk_expert_standin", "tk_swiglu_quant", "tk_balance_loss"):
         getattr(L, name).restype = ctypes.c_int32
     L.tk_map_workspace_bytes.restype = ctypes.c_size_t
+    L.tk_balance_workspace_bytes.restype = ctypes.c_size_t
     return L
 
 
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["tk_last_error", "tk_route", "tk_map_workspace_bytes", "tk_map",
                                   "tk_map_aligned", "tk_expand_quant", "tk_reduce",
-                                  "tk_expert_standin", "tk_swiglu_quant"])
+                                  "tk_expert_standin", "tk_swiglu_quant",
+                                  "tk_balance_workspace_bytes", "tk_balance_loss"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -210,3 +212,24 @@ def test_map_aligned_rejects_bad_arguments(lib):
     # T*k plus the largest padding must fit in int32 positions
     assert call(1 << 27, 8, 256, 0, 256, 1 << 24) == ARG
     assert b"padding" in lib.tk_last_error()
+
+
+def test_balance_rejects_bad_arguments(lib):
+    I = ctypes.c_int32
+    ws = ctypes.c_size_t(1 << 20)
+
+    def call(T, E, k, score, logits=FAKE, idx=FAKE, w=FAKE, wsb=ws):
+        return lib.tk_balance_loss(logits, idx, I(T), I(E), I(k), I(score), FAKE, FAKE, FAKE, w,
+                                   wsb, None)
+
+    assert call(0, 256, 8, 1) == ARG
+    assert call(16, 0, 8, 1) == ARG
+    assert call(16, 2048, 8, 1) == UNSUP
+    assert call(16, 256, 0, 1) == ARG
+    assert call(16, 256, 8, 7) == ARG
+    assert call(16, 256, 8, 1, logits=None) == ARG
+    assert call(8192, 256, 8, 1, wsb=ctypes.c_size_t(10)) == ARG
+    assert b"workspace" in lib.tk_last_error()
+    assert call(16, 256, 8, 1, w=MIS1) == ARG
+    assert lib.tk_balance_workspace_bytes(I(8192), I(256)) == 256 * 256 * 8   # 256 tiles of 32
+    assert lib.tk_balance_workspace_bytes(I(0), I(256)) == 0
