@@ -58,6 +58,20 @@ def _declare(L: ctypes.CDLL) -> ctypes.CDLL:
     L.orc_map_aligned.restype = i32
     L.orc_balance_loss.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp]
     L.orc_balance_loss.restype = i32
+    L.orc_pow2_scale_e4m3.argtypes = [f32]
+    L.orc_pow2_scale_e4m3.restype = f32
+    L.orc_quant_1x128.argtypes = [vp, i64, i32, i32, vp, vp]
+    L.orc_quant_1x128.restype = None
+    L.orc_quant_128x128.argtypes = [vp, i64, i32, vp, vp]
+    L.orc_quant_128x128.restype = None
+    L.orc_quant_per_channel.argtypes = [vp, i64, i32, vp, vp]
+    L.orc_quant_per_channel.restype = None
+    L.orc_quant_fp4_1x32.argtypes = [vp, i64, i32, vp, vp]
+    L.orc_quant_fp4_1x32.restype = None
+    L.orc_e2m1_to_f64.argtypes = [ctypes.c_uint8]
+    L.orc_e2m1_to_f64.restype = f64
+    L.orc_e2m1_from_f32_n.argtypes = [vp, i64, vp]
+    L.orc_e2m1_from_f32_n.restype = None
     L.orc_expand.argtypes = [vp, i32, i32, i32, vp, i32, i64, vp, vp]
     L.orc_expand.restype = i32
     L.orc_quant_row.argtypes = [vp, i32, vp, vp]
@@ -306,3 +320,50 @@ def swiglu_quant(h, I: int, row_w=None):
     if lib().orc_swiglu_quant(_p(h), rows, I, _p(rw), _p(q), _p(sc)) != 0:
         raise ValueError("oracle swiglu_quant: unsupported arguments")
     return q, sc
+
+
+# ------------------------------------------------ next: quant granularities --
+QUANT_FP8_1X128, QUANT_FP8_1X128_POW2, QUANT_FP8_128X128, QUANT_FP8_PER_CHANNEL, QUANT_FP4_1X32 = range(5)
+
+
+def quant(x, mode: int):
+    """Quantise a bf16 matrix (uint16 bits, (rows, cols)); returns (codes, scales)."""
+    x = _c(x, np.uint16)
+    rows, cols = x.shape
+    L = lib()
+    if mode in (QUANT_FP8_1X128, QUANT_FP8_1X128_POW2):
+        q = np.empty((rows, cols), np.uint8)
+        sc = np.empty((rows, cols // 128), np.float32)
+        L.orc_quant_1x128(_p(x), rows, cols, int(mode == QUANT_FP8_1X128_POW2), _p(q), _p(sc))
+    elif mode == QUANT_FP8_128X128:
+        q = np.empty((rows, cols), np.uint8)
+        sc = np.empty(((rows + 127) // 128, cols // 128), np.float32)
+        L.orc_quant_128x128(_p(x), rows, cols, _p(q), _p(sc))
+    elif mode == QUANT_FP8_PER_CHANNEL:
+        q = np.empty((rows, cols), np.uint8)
+        sc = np.empty(cols, np.float32)
+        L.orc_quant_per_channel(_p(x), rows, cols, _p(q), _p(sc))
+    elif mode == QUANT_FP4_1X32:
+        q = np.empty((rows, cols // 2), np.uint8)
+        sc = np.empty((rows, cols // 32), np.float32)
+        L.orc_quant_fp4_1x32(_p(x), rows, cols, _p(q), _p(sc))
+    else:
+        raise ValueError(f"unknown quant mode {mode}")
+    return q, sc
+
+
+def pow2_scale_e4m3(amax: float) -> float:
+    return float(lib().orc_pow2_scale_e4m3(float(amax)))
+
+
+def e2m1_from_f32(v) -> np.ndarray:
+    v = _c(v, np.float32)
+    q = np.empty(v.shape, np.uint8)
+    lib().orc_e2m1_from_f32_n(_p(v), v.size, _p(q))
+    return q
+
+
+def e2m1_to_f64(q) -> np.ndarray:
+    q = _c(q, np.uint8)
+    table = np.array([lib().orc_e2m1_to_f64(c) for c in range(16)], np.float64)
+    return table[q & 15]

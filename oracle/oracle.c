@@ -635,6 +635,150 @@ int orc_swiglu_f32(const uint16_t* h, int64_t rows, int I, const float* row_w, f
     return 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Other granularities of the quantisation codec (TileKernels' quant/ module */
+/* lists per-token, per-block and per-channel FP8 and FP4).  Inputs are bf16 */
+/* matrices (rows, cols), row-major.                                          */
+/* ------------------------------------------------------------------------ */
+
+/* Power-of-two block scale for FP8: the smallest 2^e with 448 * 2^e >= amax */
+/* (amax clamped >= 1e-4), found from amax's binary exponent: with            */
+/* amax = m * 2^x, m in [0.5, 1) and 448 = 0.875 * 2^9,                       */
+/* amax / 448 <= 2^(x-9) exactly when m <= 0.875.                             */
+float orc_pow2_scale_e4m3(float amax)
+{
+    if (amax < 1e-4f) amax = 1e-4f;
+    int x;
+    const float m = frexpf(amax, &x);
+    return ldexpf(1.0f, m <= 0.875f ? x - 9 : x - 8);
+}
+
+/* Per-token 1x128 FP8 of a (rows, cols) matrix, cols % 128 == 0; scales     */
+/* (rows, cols/128).  pow2 = 0: scale = RN32(amax/448) (orc_quant_row);       */
+/* pow2 = 1: scale = orc_pow2_scale_e4m3(amax), q = E4M3(x * (1/scale))       */
+/* (exact: a power of two).                                                   */
+void orc_quant_1x128(const uint16_t* x, int64_t rows, int cols, int pow2, uint8_t* q,
+                     float* scales)
+{
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint16_t* xr = x + (size_t)r * cols;
+        uint8_t* qr = q + (size_t)r * cols;
+        float* sr = scales + (size_t)r * (cols / 128);
+        if (!pow2) { orc_quant_row(xr, cols, qr, sr); continue; }
+        for (int b = 0; b < cols / 128; ++b) {
+            float amax = 0.0f;
+            for (int c = b * 128; c < b * 128 + 128; ++c) {
+                const float a = fabsf(orc_bf16_to_f32(xr[c]));
+                if (a > amax) amax = a;
+            }
+            const float scale = orc_pow2_scale_e4m3(amax);
+            sr[b] = scale;
+            for (int c = b * 128; c < b * 128 + 128; ++c)
+                qr[c] = orc_e4m3_from_f32(orc_bf16_to_f32(xr[c]) / scale);
+        }
+    }
+}
+
+/* Per-block 128x128 FP8 (weights): one scale per tile of 128 rows x 128    */
+/* columns (the last tile row may be shorter), scale = RN32(max(amax,1e-4)/448)*/
+/* q = E4M3(RN32(x/scale)).  cols % 128 == 0; scales (ceil(rows/128), cols/128)*/
+void orc_quant_128x128(const uint16_t* x, int64_t rows, int cols, uint8_t* q, float* scales)
+{
+    const int64_t tr = (rows + 127) / 128;
+    for (int64_t bi = 0; bi < tr; ++bi)
+        for (int bj = 0; bj < cols / 128; ++bj) {
+            const int64_t r1 = (bi + 1) * 128 < rows ? (bi + 1) * 128 : rows;
+            float amax = 0.0f;
+            for (int64_t r = bi * 128; r < r1; ++r)
+                for (int c = bj * 128; c < bj * 128 + 128; ++c) {
+                    const float a = fabsf(orc_bf16_to_f32(x[(size_t)r * cols + c]));
+                    if (a > amax) amax = a;
+                }
+            if (amax < 1e-4f) amax = 1e-4f;
+            const float scale = amax / 448.0f;
+            scales[(size_t)bi * (cols / 128) + bj] = scale;
+            for (int64_t r = bi * 128; r < r1; ++r)
+                for (int c = bj * 128; c < bj * 128 + 128; ++c)
+                    q[(size_t)r * cols + c] = orc_e4m3_from_f32(orc_bf16_to_f32(x[(size_t)r * cols + c]) / scale);
+        }
+}
+
+/* Per-channel FP8: one scale per column over all rows,                      */
+/* scale = RN32(max(amax,1e-4)/448), q = E4M3(RN32(x/scale)); scales (cols).  */
+void orc_quant_per_channel(const uint16_t* x, int64_t rows, int cols, uint8_t* q, float* scales)
+{
+    for (int c = 0; c < cols; ++c) {
+        float amax = 0.0f;
+        for (int64_t r = 0; r < rows; ++r) {
+            const float a = fabsf(orc_bf16_to_f32(x[(size_t)r * cols + c]));
+            if (a > amax) amax = a;
+        }
+        if (amax < 1e-4f) amax = 1e-4f;
+        scales[c] = amax / 448.0f;
+    }
+    for (int64_t r = 0; r < rows; ++r)
+        for (int c = 0; c < cols; ++c)
+            q[(size_t)r * cols + c] = orc_e4m3_from_f32(orc_bf16_to_f32(x[(size_t)r * cols + c]) / scales[c]);
+}
+
+/* FP4 E2M1 (OCP MX element format): sign, 2 exponent bits (bias 1), 1       */
+/* mantissa bit; magnitudes of codes 0..7 = 0, 0.5, 1, 1.5, 2, 3, 4, 6.       */
+double orc_e2m1_to_f64(uint8_t c)
+{
+    static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    const double m = mag[c & 7];
+    return (c & 8) ? -m : m;
+}
+
+/* Nearest E2M1 value, ties to the even code (= even mantissa bit), sign kept,*/
+/* magnitudes beyond 6 saturate to 6.  NaN gives +-6 (no NaN code exists).   */
+uint8_t orc_e2m1_from_f32(float v)
+{
+    const uint8_t sign = signbit(v) ? 8 : 0;
+    const double a = fabs((double)v);
+    if (isnan(v) || a >= 6.0) return sign | 7;
+    int best = 0;
+    for (int c = 1; c < 8; ++c) {
+        const double dc = fabs(a - orc_e2m1_to_f64((uint8_t)c));
+        const double db = fabs(a - orc_e2m1_to_f64((uint8_t)best));
+        if (dc < db || (dc == db && (c & 1) == 0)) best = c;
+    }
+    return sign | (uint8_t)best;
+}
+
+/* FP4 with 1x32 blocks and power-of-two scales (OCP MX-style): per block,   */
+/* amax clamped >= 1e-4, X = 2^(floor(log2 amax) - 2) (2 = the largest E2M1  */
+/* exponent), codes E2M1(x / X) (exact division), saturating.  cols % 32 == 0;*/
+/* codes two per byte, column 2i in the low nibble; q (rows, cols/2),        */
+/* scales (rows, cols/32) as fp32 powers of two.                              */
+void orc_quant_fp4_1x32(const uint16_t* x, int64_t rows, int cols, uint8_t* q, float* scales)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        for (int b = 0; b < cols / 32; ++b) {
+            const uint16_t* xb = x + (size_t)r * cols + (size_t)b * 32;
+            float amax = 0.0f;
+            for (int c = 0; c < 32; ++c) {
+                const float a = fabsf(orc_bf16_to_f32(xb[c]));
+                if (a > amax) amax = a;
+            }
+            if (amax < 1e-4f) amax = 1e-4f;
+            int e;
+            frexpf(amax, &e);                        /* amax = m * 2^e, m in [0.5, 1) */
+            const float scale = ldexpf(1.0f, (e - 1) - 2);
+            scales[(size_t)r * (cols / 32) + b] = scale;
+            for (int c = 0; c < 32; c += 2) {
+                const uint8_t lo = orc_e2m1_from_f32(orc_bf16_to_f32(xb[c]) / scale);
+                const uint8_t hi = orc_e2m1_from_f32(orc_bf16_to_f32(xb[c + 1]) / scale);
+                q[(size_t)r * (cols / 2) + (size_t)b * 16 + c / 2] = (uint8_t)(lo | (hi << 4));
+            }
+        }
+}
+
+void orc_e2m1_from_f32_n(const float* v, int64_t n, uint8_t* q)
+{
+    for (int64_t i = 0; i < n; ++i) q[i] = orc_e2m1_from_f32(v[i]);
+}
+
 /* Element-wise helpers over arrays, for the codec pins. */
 void orc_e4m3_from_f32_n(const float* v, int64_t n, uint8_t* q)
 {
