@@ -218,6 +218,30 @@ def bench_map_balance(tk, torch, logits, idx, steps):
                              "bound": "latency (two dependent launches)"}}
 
 
+def bench_quant(tk, torch, x, steps):
+    """Each codec granularity on the step's hidden states (8192 x 7168 bf16)."""
+    out = {}
+    names = {tk.TK_QUANT_FP8_1X128: "quant_fp8_1x128", tk.TK_QUANT_FP8_1X128_POW2: "quant_fp8_1x128_pow2",
+             tk.TK_QUANT_FP8_128X128: "quant_fp8_128x128",
+             tk.TK_QUANT_FP8_PER_CHANNEL: "quant_fp8_per_channel",
+             tk.TK_QUANT_FP4_1X32: "quant_fp4_1x32"}
+    for mode, name in names.items():
+        q, s = tk.tk_quant(x, mode)
+        need = int(tk.library().tk_quant_workspace_bytes(T, H, mode))
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device) if need else None
+        us = _time_calls(torch, lambda: tk.tk_quant(x, mode, q, s, ws), min(steps, 20), (q, s))
+        nbytes = T * H * 2 + q.numel() + s.numel() * 4
+        if mode == tk.TK_QUANT_FP8_PER_CHANNEL:
+            nbytes += T * H * 2          # two passes over x: column maxima, then codes
+        out[name] = {"workload": f"x bf16 ({T}, {H})", "us_per_call": round(us, 2),
+                     "timing": "HIP graph of the calls",
+                     "roofline": {"bound": "hbm", "achieved": round(nbytes / us / 1e3, 1),
+                                  "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                  "frac": round(nbytes / us / 1e3 / PEAK_HBM_GBPS, 4),
+                                  "algorithmic_bytes": nbytes}}
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -329,7 +353,8 @@ def main() -> int:
 
     next_rows = {"swiglu_quant_fp8": bench_swiglu(tk, torch, y, offsets[E:], row_src, pos, w,
                                                   args.steps),
-                 **bench_map_balance(tk, torch, logits, idx, args.steps)}
+                 **bench_map_balance(tk, torch, logits, idx, args.steps),
+                 **bench_quant(tk, torch, x, args.steps)}
 
     ms_per_step = total_ms / args.steps
     value = T / (ms_per_step * 1e-3)

@@ -10,6 +10,11 @@
  *                    optionally fused 1x128 FP8 E4M3 quant    scales])
  *   tk_reduce        weighted combine back to tokens        (rows, w -> out)
  *
+ * quantisation at other granularities (power-of-two scales, 128x128 tiles,
+ * per channel, FP4),
+ *
+ *   tk_quant         bf16 matrix -> FP8 / FP4 codes + scales
+ *
  * per-expert load statistics and the load-balance loss,
  *
  *   tk_balance_loss  f, P and sum_e f_e P_e of one batch    (logits, idx ->
@@ -239,6 +244,52 @@ tk_status tk_expand_quant(const void* x_bf16, int32_t T, int32_t H, int32_t k,
  */
 tk_status tk_reduce(const void* y_bf16, int64_t rows, const int32_t* pos, const float* topk_w,
                     int32_t T, int32_t k, int32_t H, void* out_bf16, hipStream_t stream);
+
+/* --------------------------------------------- quantisation granularities */
+#define TK_QUANT_FP8_1X128 0        /* per-token 1x128 blocks, scale = amax/448 */
+#define TK_QUANT_FP8_1X128_POW2 1   /* 1x128 blocks, power-of-two scales */
+#define TK_QUANT_FP8_128X128 2      /* one scale per 128x128 tile */
+#define TK_QUANT_FP8_PER_CHANNEL 3  /* one scale per column */
+#define TK_QUANT_FP4_1X32 4         /* E2M1, 1x32 blocks, power-of-two scales */
+
+/* Bytes of device workspace tk_quant needs (non-zero only for per-channel). */
+size_t tk_quant_workspace_bytes(int64_t rows, int32_t cols, int32_t mode);
+
+/*
+ * tk_quant -- quantise a bf16 matrix x (rows, cols) at one of the
+ * granularities of TileKernels' quant/ module ("刚刚！DeepSeek开源高性能GPU算子库
+ * TileKernels", item quant/: per-token, per-block and per-channel FP8;
+ * "剛剛，DeepSeek開始頻繁更新：Tile Kernels、DeepEP V2", feature list: FP8 and FP4
+ * conversion).  amax is the block's largest |x| (bf16 -> fp32 exact), clamped
+ * to >= 1e-4.  FP8 codes are OCP E4M3FN of RN32(x / scale), nearest even,
+ * sign kept, saturating at 448.
+ *   TK_QUANT_FP8_1X128       blocks of 128 columns of one row; scale =
+ *                            RN32(amax/448) -- tk_expand_quant's codec.
+ *                            out (rows, cols), scales (rows, cols/128)
+ *   TK_QUANT_FP8_1X128_POW2  the same blocks; scale = the smallest power of
+ *                            two with 448*scale >= amax (UE8M0-representable)
+ *   TK_QUANT_FP8_128X128     tiles of 128 rows x 128 columns (the last tile
+ *                            row may be shorter); scale = RN32(amax/448).
+ *                            out (rows, cols), scales (ceil(rows/128), cols/128)
+ *   TK_QUANT_FP8_PER_CHANNEL one block per column, over all rows; scale =
+ *                            RN32(amax/448).  out (rows, cols), scales (cols);
+ *                            needs tk_quant_workspace_bytes of workspace
+ *   TK_QUANT_FP4_1X32        FP4 E2M1 (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6;
+ *                            nearest, ties to the even code, sign kept,
+ *                            saturating at 6) of x / scale over blocks of 32
+ *                            columns; scale = 2^(floor(log2 amax) - 2) (the
+ *                            OCP MX shared-exponent rule for E2M1).  Two
+ *                            codes per byte, column 2i in the low nibble:
+ *                            out (rows, cols/2); scales (rows, cols/32), fp32
+ *                            powers of two.
+ * cols must be a positive multiple of 128 (FP8 block and tile modes), 8
+ * (per-channel) or 32 (FP4).  Inputs are finite.
+ *
+ * x_bf16, out, scales  device, 16-byte aligned
+ * workspace            device, 16-byte aligned, per-channel only (else NULL)
+ */
+tk_status tk_quant(const void* x_bf16, int64_t rows, int32_t cols, int32_t mode, void* out,
+                   float* scales, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------ load balance */
 /* Bytes of device workspace tk_balance_loss needs for T tokens and E experts. */

@@ -14,6 +14,7 @@ step of the path runs in the library's HIP kernels; there is no fallback.
     tk_expert_standin(xq, scales, n_rows, mult) -> y
     tk_swiglu_quant(h, I, n_rows, row_src, pos, topk_w) -> (out, scales)
     tk_balance_loss(logits, topk_idx, score)   -> (f, P, loss)
+    tk_quant(x, mode)                          -> (codes, scales)
 """
 from __future__ import annotations
 
@@ -30,6 +31,8 @@ TK_OK, TK_ERR_ARG, TK_ERR_UNSUPPORTED, TK_ERR_DEVICE = 0, -1, -2, -3
 TK_MAX_EXPERTS, TK_MAX_TOPK = 1024, 32
 TK_SCORE_SOFTMAX, TK_SCORE_SIGMOID = 0, 1
 TK_EXPAND_BF16, TK_EXPAND_FP8_E4M3_1X128 = 0, 1
+(TK_QUANT_FP8_1X128, TK_QUANT_FP8_1X128_POW2, TK_QUANT_FP8_128X128, TK_QUANT_FP8_PER_CHANNEL,
+ TK_QUANT_FP4_1X32) = range(5)
 
 
 class TkError(RuntimeError):
@@ -95,6 +98,10 @@ def library() -> ctypes.CDLL:
         L.tk_balance_workspace_bytes.restype = sz
         L.tk_balance_loss.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
         L.tk_balance_loss.restype = i32
+        L.tk_quant_workspace_bytes.argtypes = [i64, i32, i32]
+        L.tk_quant_workspace_bytes.restype = sz
+        L.tk_quant.argtypes = [vp, i64, i32, i32, vp, vp, vp, sz, vp]
+        L.tk_quant.restype = i32
         _lib = L
     return _lib
 
@@ -299,3 +306,39 @@ def tk_balance_loss(logits: torch.Tensor, topk_idx: torch.Tensor, score: int,
         _ptr(logits), _ptr(topk_idx), T, E, k, score, _ptr(f), _ptr(P), _ptr(loss),
         _ptr(workspace), workspace.numel(), _stream(logits)))
     return f, P, loss
+
+
+def _quant_shapes(rows: int, cols: int, mode: int):
+    if mode in (TK_QUANT_FP8_1X128, TK_QUANT_FP8_1X128_POW2):
+        return (rows, cols), torch.uint8, (rows, cols // 128)
+    if mode == TK_QUANT_FP8_128X128:
+        return (rows, cols), torch.uint8, ((rows + 127) // 128, cols // 128)
+    if mode == TK_QUANT_FP8_PER_CHANNEL:
+        return (rows, cols), torch.uint8, (cols,)
+    if mode == TK_QUANT_FP4_1X32:
+        return (rows, cols // 2), torch.uint8, (rows, cols // 32)
+    raise ValueError(f"unknown quant mode {mode}")
+
+
+def tk_quant(x: torch.Tensor, mode: int, out: torch.Tensor | None = None,
+             scales: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Quantise a bf16 matrix at the granularity `mode` (TK_QUANT_*)."""
+    _dev(x, "x", torch.bfloat16, 2)
+    rows, cols = x.shape
+    oshape, odt, sshape = _quant_shapes(rows, cols, mode)
+    if out is None:
+        out = torch.empty(oshape, dtype=odt, device=x.device)
+    if scales is None:
+        scales = torch.empty(sshape, dtype=torch.float32, device=x.device)
+    need = int(library().tk_quant_workspace_bytes(rows, cols, mode))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _dev(out, "out", torch.uint8)
+    _dev(scales, "scales", torch.float32)
+    if workspace is not None:
+        _dev(workspace, "workspace", torch.uint8)
+    _check("tk_quant", library().tk_quant(_ptr(x), rows, cols, mode, _ptr(out), _ptr(scales),
+                                          _ptr(workspace),
+                                          0 if workspace is None else workspace.numel(),
+                                          _stream(x)))
+    return out, scales

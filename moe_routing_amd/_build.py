@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtk.so")
-SOURCES = ["api.hip", "route.hip", "map.hip", "expand.hip", "reduce.hip", "swiglu.hip", "balance.hip"]
+SOURCES = ["api.hip", "route.hip", "map.hip", "expand.hip", "reduce.hip", "swiglu.hip", "balance.hip", "quant.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -1,0 +1,327 @@
+// tk_quant: the quantisation granularities of TileKernels' quant/ module
+// ("刚刚！DeepSeek开源高性能GPU算子库TileKernels", item quant/: per-token,
+// per-block and per-channel FP8; "剛剛，DeepSeek開始頻繁更新：Tile Kernels、
+// DeepEP V2", feature list: FP8 / FP4 conversion) on a bf16 matrix
+// (rows, cols), row-major:
+//
+//   TK_QUANT_FP8_1X128       per-token 1x128 blocks, scale = RN(max(amax,1e-4)/448)
+//                            (the codec of tk_expand_quant)
+//   TK_QUANT_FP8_1X128_POW2  same blocks, scale = the smallest power of two
+//                            with 448*scale >= max(amax, 1e-4)
+//   TK_QUANT_FP8_128X128     one scale per 128x128 tile (weights)
+//   TK_QUANT_FP8_PER_CHANNEL one scale per column over all rows
+//   TK_QUANT_FP4_1X32        E2M1 codes (two per byte, even column in the low
+//                            nibble), 1x32 blocks, scale 2^(floor(log2 amax)-2)
+//
+// Kernels:
+//  - 1x128 (and pow2): one wave per (row, 1024 columns), 16 columns per lane,
+//    a 128-column block per 8 lanes (amax by a 3-step DPP butterfly).
+//  - 128x128: one 256-thread workgroup per tile; each thread holds an 8x8
+//    patch (eight 16-byte row loads), the tile amax is a DPP wave max then an
+//    LDS step over the four waves.
+//  - per-channel: pass 1, one thread per 8 columns per chunk of 128 rows
+//    writes partial column maxima to the workspace; pass 2, one thread per
+//    8 columns per block of 64 rows takes the maximum over the chunks (max
+//    is exact in any order), forms the scales and quantises.
+//  - FP4: one wave per (row, 512 columns), 8 columns per lane, a 32-column
+//    block per 4 lanes; E2M1 encoding by comparison with the midpoints
+//    between neighbouring values (ties to the even code).
+// Codes are written with streaming stores; the E4M3 quotient is the shared
+// Markstein-corrected one, exact for power-of-two scales.
+#include "tk_internal.h"
+
+namespace {
+
+constexpr int kPcRowsPerChunk = 128;   // rows per partial-maximum chunk (per-channel)
+constexpr int kPcRowsPerBlock = 64;    // rows per quantising block (per-channel)
+
+__device__ __forceinline__ float pow2_scale_e4m3(float amax)
+{
+    amax = fmaxf(amax, 1e-4f);
+    int x;
+    const float m = __builtin_frexpf(amax, &x);
+    return __builtin_ldexpf(1.0f, m <= 0.875f ? x - 9 : x - 8);
+}
+
+__device__ __forceinline__ tk::u32x4 quant16_e4m3(const float (&v)[16], float scale)
+{
+    const float inv = 1.0f / scale;
+    tk::u32x4 q;
+    q.x = tk::pack_fp8x4(tk::fp8_quotient(v[0], scale, inv), tk::fp8_quotient(v[1], scale, inv),
+                         tk::fp8_quotient(v[2], scale, inv), tk::fp8_quotient(v[3], scale, inv));
+    q.y = tk::pack_fp8x4(tk::fp8_quotient(v[4], scale, inv), tk::fp8_quotient(v[5], scale, inv),
+                         tk::fp8_quotient(v[6], scale, inv), tk::fp8_quotient(v[7], scale, inv));
+    q.z = tk::pack_fp8x4(tk::fp8_quotient(v[8], scale, inv), tk::fp8_quotient(v[9], scale, inv),
+                         tk::fp8_quotient(v[10], scale, inv), tk::fp8_quotient(v[11], scale, inv));
+    q.w = tk::pack_fp8x4(tk::fp8_quotient(v[12], scale, inv), tk::fp8_quotient(v[13], scale, inv),
+                         tk::fp8_quotient(v[14], scale, inv), tk::fp8_quotient(v[15], scale, inv));
+    return q;
+}
+
+// eight bf16 (one 16-byte word) -> fp32
+__device__ __forceinline__ void unpack8(tk::u32x4 w, float* v)
+{
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = tk::bf16_lo(ws[i]);
+        v[2 * i + 1] = tk::bf16_hi(ws[i]);
+    }
+}
+
+// ------------------------------------------------------------------ 1x128
+template <bool POW2>
+__global__ __launch_bounds__(tk::kBlock) void quant_1x128_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int cols, int chunks, uint8_t* __restrict__ q,
+    float* __restrict__ scales)
+{
+    const int lane = threadIdx.x & (tk::kWave - 1);
+    const int64_t u = static_cast<int64_t>(blockIdx.x) * tk::kWavesPerBlock +
+                      tk::uniform(threadIdx.x / tk::kWave);
+    if (u >= rows * chunks) return;
+    const int64_t r = u / chunks;
+    const int col = static_cast<int>(u - r * chunks) * 1024 + lane * 16;
+    const bool active = col < cols;
+    tk::u32x4 a = tk::u32x4{0u, 0u, 0u, 0u}, b = a;
+    if (active) {
+        a = tk::load_stream(x + static_cast<size_t>(r) * cols + col);
+        b = tk::load_stream(x + static_cast<size_t>(r) * cols + col + 8);
+    }
+    float v[16];
+    unpack8(a, v);
+    unpack8(b, v + 8);
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = tk::max_run8(amax);
+    const float scale = POW2 ? pow2_scale_e4m3(amax) : fmaxf(amax, 1e-4f) / 448.0f;
+    const tk::u32x4 code = quant16_e4m3(v, scale);
+    if (active) {
+        tk::store_stream(q + static_cast<size_t>(r) * cols + col, code);
+        if ((lane & 7) == 0) scales[static_cast<size_t>(r) * (cols / 128) + col / 128] = scale;
+    }
+}
+
+// ---------------------------------------------------------------- 128x128
+__global__ __launch_bounds__(tk::kBlock) void quant_128x128_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int cols, uint8_t* __restrict__ q,
+    float* __restrict__ scales)
+{
+    __shared__ float wave_max[tk::kWavesPerBlock];
+    const int tiles_c = cols / 128;
+    const int64_t tr = blockIdx.x / tiles_c;
+    const int tc = static_cast<int>(blockIdx.x - tr * tiles_c);
+    // thread -> 8 rows x 8 columns of the tile
+    const int cg = threadIdx.x & 15, rg = threadIdx.x >> 4;
+    const int col = tc * 128 + cg * 8;
+    const int64_t r0 = tr * 128 + rg * 8;
+    float v[8][8];
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        tk::u32x4 w = tk::u32x4{0u, 0u, 0u, 0u};
+        if (r0 + i < rows) w = tk::load_stream(x + static_cast<size_t>(r0 + i) * cols + col);
+        unpack8(w, v[i]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[i][j]));
+    }
+    amax = tk::max_wave_f32(amax);
+    if ((threadIdx.x & (tk::kWave - 1)) == 0) wave_max[threadIdx.x / tk::kWave] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
+    const float scale = fmaxf(amax, 1e-4f) / 448.0f;
+    const float inv = 1.0f / scale;
+    if (threadIdx.x == 0) scales[tr * tiles_c + tc] = scale;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if (r0 + i >= rows) break;
+        uint2 o;
+        o.x = tk::pack_fp8x4(tk::fp8_quotient(v[i][0], scale, inv), tk::fp8_quotient(v[i][1], scale, inv),
+                             tk::fp8_quotient(v[i][2], scale, inv), tk::fp8_quotient(v[i][3], scale, inv));
+        o.y = tk::pack_fp8x4(tk::fp8_quotient(v[i][4], scale, inv), tk::fp8_quotient(v[i][5], scale, inv),
+                             tk::fp8_quotient(v[i][6], scale, inv), tk::fp8_quotient(v[i][7], scale, inv));
+        *reinterpret_cast<uint2*>(q + static_cast<size_t>(r0 + i) * cols + col) = o;
+    }
+}
+
+// ------------------------------------------------------------ per-channel
+// partial[chunk][c] = max |x[r, c]| over the chunk's rows
+__global__ __launch_bounds__(tk::kBlock) void quant_pc_partial_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int cols, float* __restrict__ partial)
+{
+    const int col = (blockIdx.x * tk::kBlock + threadIdx.x) * 8;
+    if (col >= cols) return;
+    const int64_t chunk = blockIdx.y;
+    const int64_t r0 = chunk * kPcRowsPerChunk;
+    const int64_t r1 = r0 + kPcRowsPerChunk < rows ? r0 + kPcRowsPerChunk : rows;
+    float m[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m[j] = 0.f;
+    for (int64_t r = r0; r < r1; ++r) {
+        float v[8];
+        unpack8(tk::load16(x + static_cast<size_t>(r) * cols + col), v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) m[j] = fmaxf(m[j], fabsf(v[j]));
+    }
+    float* p = partial + static_cast<size_t>(chunk) * cols + col;
+    *reinterpret_cast<float4*>(p) = make_float4(m[0], m[1], m[2], m[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(m[4], m[5], m[6], m[7]);
+}
+
+__global__ __launch_bounds__(tk::kBlock) void quant_pc_apply_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int cols, int n_chunks,
+    const float* __restrict__ partial, uint8_t* __restrict__ q, float* __restrict__ scales)
+{
+    const int col = (blockIdx.x * tk::kBlock + threadIdx.x) * 8;
+    if (col >= cols) return;
+    float s[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s[j] = 0.f;
+    for (int ch = 0; ch < n_chunks; ++ch) {
+        const float* p = partial + static_cast<size_t>(ch) * cols + col;
+        const float4 a = *reinterpret_cast<const float4*>(p);
+        const float4 b = *reinterpret_cast<const float4*>(p + 4);
+        s[0] = fmaxf(s[0], a.x); s[1] = fmaxf(s[1], a.y); s[2] = fmaxf(s[2], a.z); s[3] = fmaxf(s[3], a.w);
+        s[4] = fmaxf(s[4], b.x); s[5] = fmaxf(s[5], b.y); s[6] = fmaxf(s[6], b.z); s[7] = fmaxf(s[7], b.w);
+    }
+    float inv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        s[j] = fmaxf(s[j], 1e-4f) / 448.0f;
+        inv[j] = 1.0f / s[j];
+    }
+    if (blockIdx.y == 0) {
+        *reinterpret_cast<float4*>(scales + col) = make_float4(s[0], s[1], s[2], s[3]);
+        *reinterpret_cast<float4*>(scales + col + 4) = make_float4(s[4], s[5], s[6], s[7]);
+    }
+    const int64_t r0 = static_cast<int64_t>(blockIdx.y) * kPcRowsPerBlock;
+    const int64_t r1 = r0 + kPcRowsPerBlock < rows ? r0 + kPcRowsPerBlock : rows;
+    for (int64_t r = r0; r < r1; ++r) {
+        float v[8];
+        unpack8(tk::load_stream(x + static_cast<size_t>(r) * cols + col), v);
+        uint2 o;
+        o.x = tk::pack_fp8x4(tk::fp8_quotient(v[0], s[0], inv[0]), tk::fp8_quotient(v[1], s[1], inv[1]),
+                             tk::fp8_quotient(v[2], s[2], inv[2]), tk::fp8_quotient(v[3], s[3], inv[3]));
+        o.y = tk::pack_fp8x4(tk::fp8_quotient(v[4], s[4], inv[4]), tk::fp8_quotient(v[5], s[5], inv[5]),
+                             tk::fp8_quotient(v[6], s[6], inv[6]), tk::fp8_quotient(v[7], s[7], inv[7]));
+        *reinterpret_cast<uint2*>(q + static_cast<size_t>(r) * cols + col) = o;
+    }
+}
+
+// ------------------------------------------------------------------- FP4
+// E2M1 code of v (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6): the number of
+// midpoints below |v|, with a tie going to the even code, saturating at 6.
+__device__ __forceinline__ uint32_t e2m1_code(float v)
+{
+    const float a = fabsf(v);
+    const uint32_t c = static_cast<uint32_t>(a > 0.25f) + static_cast<uint32_t>(a >= 0.75f) +
+                       static_cast<uint32_t>(a > 1.25f) + static_cast<uint32_t>(a >= 1.75f) +
+                       static_cast<uint32_t>(a > 2.5f) + static_cast<uint32_t>(a >= 3.5f) +
+                       static_cast<uint32_t>(a > 5.0f);
+    return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+__global__ __launch_bounds__(tk::kBlock) void quant_fp4_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int cols, int chunks, uint8_t* __restrict__ q,
+    float* __restrict__ scales)
+{
+    const int lane = threadIdx.x & (tk::kWave - 1);
+    const int64_t u = static_cast<int64_t>(blockIdx.x) * tk::kWavesPerBlock +
+                      tk::uniform(threadIdx.x / tk::kWave);
+    if (u >= rows * chunks) return;
+    const int64_t r = u / chunks;
+    const int col = static_cast<int>(u - r * chunks) * 512 + lane * 8;
+    const bool active = col < cols;   // cols % 32 == 0: 4-lane groups wholly in or out
+    tk::u32x4 w = tk::u32x4{0u, 0u, 0u, 0u};
+    if (active) w = tk::load_stream(x + static_cast<size_t>(r) * cols + col);
+    float v[8];
+    unpack8(w, v);
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = fmaxf(amax, tk::dpp_f32<tk::kQuadXor1>(amax));
+    amax = fmaxf(amax, tk::dpp_f32<tk::kQuadXor2>(amax));   // one 32-column block per quad
+    amax = fmaxf(amax, 1e-4f);
+    int e;
+    __builtin_frexpf(amax, &e);
+    const float scale = __builtin_ldexpf(1.0f, e - 3);     // 2^(floor(log2 amax) - 2)
+    const float inv = __builtin_ldexpf(1.0f, 3 - e);       // exact
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) packed |= e2m1_code(v[i] * inv) << (4 * i);
+    if (active) {
+        *reinterpret_cast<uint32_t*>(q + static_cast<size_t>(r) * (cols / 2) + col / 2) = packed;
+        if ((lane & 3) == 0) scales[static_cast<size_t>(r) * (cols / 32) + col / 32] = scale;
+    }
+}
+
+unsigned blocks_for(int64_t waves) { return static_cast<unsigned>((waves + tk::kWavesPerBlock - 1) / tk::kWavesPerBlock); }
+
+}  // namespace
+
+TK_EXPORT size_t tk_quant_workspace_bytes(int64_t rows, int32_t cols, int32_t mode)
+{
+    if (mode != TK_QUANT_FP8_PER_CHANNEL || rows <= 0 || cols <= 0) return 0;
+    const int64_t n_chunks = (rows + kPcRowsPerChunk - 1) / kPcRowsPerChunk;
+    return static_cast<size_t>(n_chunks) * static_cast<size_t>(cols) * sizeof(float);
+}
+
+TK_EXPORT tk_status tk_quant(const void* x_bf16, int64_t rows, int32_t cols, int32_t mode,
+                             void* out, float* scales, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream)
+{
+    using tk::fail;
+    if (rows < 0) return fail(TK_ERR_ARG, "tk_quant: rows < 0");
+    int align = 0;
+    switch (mode) {
+    case TK_QUANT_FP8_1X128: case TK_QUANT_FP8_1X128_POW2: case TK_QUANT_FP8_128X128: align = 128; break;
+    case TK_QUANT_FP8_PER_CHANNEL: align = 8; break;
+    case TK_QUANT_FP4_1X32: align = 32; break;
+    default: return fail(TK_ERR_ARG, "tk_quant: unknown mode %d", mode);
+    }
+    if (cols <= 0 || cols % align != 0)
+        return fail(TK_ERR_ARG, "tk_quant: cols=%d must be a positive multiple of %d for mode %d",
+                    cols, align, mode);
+    if (rows == 0) return tk::ok();
+    if (x_bf16 == nullptr || out == nullptr || scales == nullptr)
+        return fail(TK_ERR_ARG, "tk_quant: NULL tensor pointer");
+    if (!tk::aligned16(x_bf16) || !tk::aligned16(out) || !tk::aligned16(scales))
+        return fail(TK_ERR_ARG, "tk_quant: x, out and scales must be 16-byte aligned");
+    const auto* x = static_cast<const uint16_t*>(x_bf16);
+    auto* q = static_cast<uint8_t*>(out);
+    const dim3 block(tk::kBlock);
+    hipError_t e = hipSuccess;
+    if (mode == TK_QUANT_FP8_1X128 || mode == TK_QUANT_FP8_1X128_POW2) {
+        const int chunks = (cols + 1023) / 1024;
+        const dim3 grid(blocks_for(rows * chunks));
+        e = mode == TK_QUANT_FP8_1X128_POW2
+            ? tk::launch(quant_1x128_kernel<true>, grid, block, 0, stream, x, rows, cols, chunks, q, scales)
+            : tk::launch(quant_1x128_kernel<false>, grid, block, 0, stream, x, rows, cols, chunks, q, scales);
+    } else if (mode == TK_QUANT_FP8_128X128) {
+        const int64_t tiles = (rows + 127) / 128 * (cols / 128);
+        if (tiles > INT32_MAX) return fail(TK_ERR_UNSUPPORTED, "tk_quant: too many tiles");
+        e = tk::launch(quant_128x128_kernel, dim3(static_cast<unsigned>(tiles)), block, 0, stream,
+                       x, rows, cols, q, scales);
+    } else if (mode == TK_QUANT_FP8_PER_CHANNEL) {
+        const size_t need = tk_quant_workspace_bytes(rows, cols, mode);
+        if (workspace == nullptr || workspace_bytes < need || !tk::aligned16(workspace))
+            return fail(TK_ERR_ARG, "tk_quant: per-channel needs a 16-byte aligned workspace of "
+                        "%zu bytes (got %zu)", need, workspace_bytes);
+        const int64_t n_chunks = (rows + kPcRowsPerChunk - 1) / kPcRowsPerChunk;
+        const int64_t n_blocks = (rows + kPcRowsPerBlock - 1) / kPcRowsPerBlock;
+        if (n_chunks > 65535 || n_blocks > 65535)
+            return fail(TK_ERR_UNSUPPORTED, "tk_quant: too many rows for per-channel");
+        const unsigned gx = static_cast<unsigned>((cols / 8 + tk::kBlock - 1) / tk::kBlock);
+        auto* partial = static_cast<float*>(workspace);
+        e = tk::launch(quant_pc_partial_kernel, dim3(gx, static_cast<unsigned>(n_chunks)), block, 0,
+                       stream, x, rows, cols, partial);
+        if (e != hipSuccess) return tk::launched(e, "tk_quant (per-channel maxima)");
+        e = tk::launch(quant_pc_apply_kernel, dim3(gx, static_cast<unsigned>(n_blocks)), block, 0,
+                       stream, x, rows, cols, static_cast<int>(n_chunks), partial, q, scales);
+    } else {
+        const int chunks = (cols + 511) / 512;
+        e = tk::launch(quant_fp4_kernel, dim3(blocks_for(rows * chunks)), block, 0, stream, x, rows,
+                       cols, chunks, q, scales);
+    }
+    return tk::launched(e, "tk_quant");
+}

@@ -30,10 +30,11 @@ def lib():
     L = ctypes.CDLL(LIB)
     L.tk_last_error.restype = ctypes.c_char_p
     for name in ("tk_route", "tk_map", "tk_map_aligned", "tk_expand_quant", "tk_reduce",
-                 "tk_expert_standin", "tk_swiglu_quant", "tk_balance_loss"):
+                 "tk_expert_standin", "tk_swiglu_quant", "tk_balance_loss", "tk_quant"):
         getattr(L, name).restype = ctypes.c_int32
     L.tk_map_workspace_bytes.restype = ctypes.c_size_t
     L.tk_balance_workspace_bytes.restype = ctypes.c_size_t
+    L.tk_quant_workspace_bytes.restype = ctypes.c_size_t
     return L
 
 
@@ -41,7 +42,8 @@ def test_header_declares_the_entry_points():
     assert _declared() == sorted(["tk_last_error", "tk_route", "tk_map_workspace_bytes", "tk_map",
                                   "tk_map_aligned", "tk_expand_quant", "tk_reduce",
                                   "tk_expert_standin", "tk_swiglu_quant",
-                                  "tk_balance_workspace_bytes", "tk_balance_loss"])
+                                  "tk_balance_workspace_bytes", "tk_balance_loss",
+                                  "tk_quant_workspace_bytes", "tk_quant"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -233,3 +235,24 @@ def test_balance_rejects_bad_arguments(lib):
     assert call(16, 256, 8, 1, w=MIS1) == ARG
     assert lib.tk_balance_workspace_bytes(I(8192), I(256)) == 256 * 256 * 8   # 256 tiles of 32
     assert lib.tk_balance_workspace_bytes(I(0), I(256)) == 0
+
+
+def test_quant_rejects_bad_arguments(lib):
+    I, I64 = ctypes.c_int32, ctypes.c_int64
+
+    def call(rows, cols, mode, x=FAKE, out=FAKE, sc=FAKE, ws=None, wsb=0):
+        return lib.tk_quant(x, I64(rows), I(cols), I(mode), out, sc, ws, ctypes.c_size_t(wsb), None)
+
+    assert call(-1, 256, 0) == ARG
+    assert call(4, 256, 9) == ARG
+    assert call(4, 200, 0) == ARG                 # FP8 blocks need cols % 128 == 0
+    assert call(4, 48, 4) == ARG                  # FP4 blocks need cols % 32 == 0
+    assert call(4, 12, 3) == ARG                  # per-channel needs cols % 8 == 0
+    assert call(4, 256, 0, x=None) == ARG
+    assert call(4, 256, 0, out=MIS) == ARG
+    assert call(4, 256, 3) == ARG                 # per-channel without workspace
+    assert b"workspace" in lib.tk_last_error()
+    assert call(0, 256, 0, x=None, out=None, sc=None) == 0
+    f = lib.tk_quant_workspace_bytes
+    assert f(I64(1000), I(256), I(3)) == 8 * 256 * 4      # 8 chunks of 128 rows
+    assert f(I64(1000), I(256), I(0)) == 0
