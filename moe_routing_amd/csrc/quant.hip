@@ -19,13 +19,14 @@
 //  - 128x128: one 256-thread workgroup per tile; each thread holds an 8x8
 //    patch (eight 16-byte row loads), the tile amax is a DPP wave max then an
 //    LDS step over the four waves.
-//  - per-channel: pass 1, one thread per 8 columns per chunk of 128 rows
-//    writes partial column maxima to the workspace; pass 2, one thread per
-//    8 columns per block of 64 rows takes the maximum over the chunks (max
-//    is exact in any order), forms the scales and quantises.
-//  - FP4: one wave per (row, 512 columns), 8 columns per lane, a 32-column
-//    block per 4 lanes; E2M1 encoding by comparison with the midpoints
-//    between neighbouring values (ties to the even code).
+//  - per-channel: workgroups of 256 columns x 8 row groups.  Pass 1 takes
+//    column maxima over chunks of 128 rows (16 rows per thread, 8 loads in
+//    flight, row groups combined in LDS) into the workspace; pass 2 takes
+//    the maximum over the chunks (exact in any order), forms the scales and
+//    quantises 64 rows per workgroup.
+//  - FP4: one wave per (row, 2048 columns), one 32-column block per lane
+//    (four 16-byte loads, one 16-byte store of codes); E2M1 encoding by
+//    integer rounding of the fp32 bits to one mantissa bit (ties to even).
 // Codes are written with streaming stores; the E4M3 quotient is the shared
 // Markstein-corrected one, exact for power-of-two scales.
 #include "tk_internal.h"
@@ -145,79 +146,131 @@ __global__ __launch_bounds__(tk::kBlock) void quant_128x128_kernel(
 }
 
 // ------------------------------------------------------------ per-channel
+// A workgroup covers 256 columns (32 groups of 8) and kPcRowsPerChunk rows
+// (8 row groups); maxima over its rows are combined in LDS.
+constexpr int kPcCols = 256;
+constexpr int kPcRowGroups = tk::kBlock / (kPcCols / 8);   // 8
+
 // partial[chunk][c] = max |x[r, c]| over the chunk's rows
 __global__ __launch_bounds__(tk::kBlock) void quant_pc_partial_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int cols, float* __restrict__ partial)
 {
-    const int col = (blockIdx.x * tk::kBlock + threadIdx.x) * 8;
-    if (col >= cols) return;
+    __shared__ float red[kPcRowGroups][kPcCols];
+    const int cgi = threadIdx.x & 31, rg = threadIdx.x >> 5;
+    const int col = blockIdx.x * kPcCols + cgi * 8;
+    const bool active = col < cols;
     const int64_t chunk = blockIdx.y;
-    const int64_t r0 = chunk * kPcRowsPerChunk;
-    const int64_t r1 = r0 + kPcRowsPerChunk < rows ? r0 + kPcRowsPerChunk : rows;
+    const int rows_per_group = kPcRowsPerChunk / kPcRowGroups;   // 16
+    const int64_t r0 = chunk * kPcRowsPerChunk + rg * rows_per_group;
     float m[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) m[j] = 0.f;
-    for (int64_t r = r0; r < r1; ++r) {
-        float v[8];
-        unpack8(tk::load16(x + static_cast<size_t>(r) * cols + col), v);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) m[j] = fmaxf(m[j], fabsf(v[j]));
+    for (int i0 = 0; i0 < rows_per_group; i0 += 8) {
+        tk::u32x4 w[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            w[i] = tk::u32x4{0u, 0u, 0u, 0u};
+            if (active && r0 + i0 + i < rows) w[i] = tk::load16(x + static_cast<size_t>(r0 + i0 + i) * cols + col);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float v[8];
+            unpack8(w[i], v);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) m[j] = fmaxf(m[j], fabsf(v[j]));
+        }
     }
-    float* p = partial + static_cast<size_t>(chunk) * cols + col;
-    *reinterpret_cast<float4*>(p) = make_float4(m[0], m[1], m[2], m[3]);
-    *reinterpret_cast<float4*>(p + 4) = make_float4(m[4], m[5], m[6], m[7]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) red[rg][cgi * 8 + j] = m[j];
+    __syncthreads();
+    if (rg == 0 && active) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+#pragma unroll
+            for (int g = 1; g < kPcRowGroups; ++g) m[j] = fmaxf(m[j], red[g][cgi * 8 + j]);
+        }
+        float* p = partial + static_cast<size_t>(chunk) * cols + col;
+        *reinterpret_cast<float4*>(p) = make_float4(m[0], m[1], m[2], m[3]);
+        *reinterpret_cast<float4*>(p + 4) = make_float4(m[4], m[5], m[6], m[7]);
+    }
 }
 
+// scales from the maxima over all chunks, then the codes of kPcRowsPerBlock rows
 __global__ __launch_bounds__(tk::kBlock) void quant_pc_apply_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int cols, int n_chunks,
     const float* __restrict__ partial, uint8_t* __restrict__ q, float* __restrict__ scales)
 {
-    const int col = (blockIdx.x * tk::kBlock + threadIdx.x) * 8;
-    if (col >= cols) return;
+    __shared__ float red[kPcRowGroups][kPcCols];
+    const int cgi = threadIdx.x & 31, rg = threadIdx.x >> 5;
+    const int col = blockIdx.x * kPcCols + cgi * 8;
+    const bool active = col < cols;
     float s[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) s[j] = 0.f;
-    for (int ch = 0; ch < n_chunks; ++ch) {
-        const float* p = partial + static_cast<size_t>(ch) * cols + col;
-        const float4 a = *reinterpret_cast<const float4*>(p);
-        const float4 b = *reinterpret_cast<const float4*>(p + 4);
-        s[0] = fmaxf(s[0], a.x); s[1] = fmaxf(s[1], a.y); s[2] = fmaxf(s[2], a.z); s[3] = fmaxf(s[3], a.w);
-        s[4] = fmaxf(s[4], b.x); s[5] = fmaxf(s[5], b.y); s[6] = fmaxf(s[6], b.z); s[7] = fmaxf(s[7], b.w);
+    if (active) {
+        for (int ch = rg; ch < n_chunks; ch += kPcRowGroups) {   // row group g takes chunks g, g+8, ...
+            const float* p = partial + static_cast<size_t>(ch) * cols + col;
+            const float4 a = *reinterpret_cast<const float4*>(p);
+            const float4 b = *reinterpret_cast<const float4*>(p + 4);
+            s[0] = fmaxf(s[0], a.x); s[1] = fmaxf(s[1], a.y); s[2] = fmaxf(s[2], a.z); s[3] = fmaxf(s[3], a.w);
+            s[4] = fmaxf(s[4], b.x); s[5] = fmaxf(s[5], b.y); s[6] = fmaxf(s[6], b.z); s[7] = fmaxf(s[7], b.w);
+        }
     }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) red[rg][cgi * 8 + j] = s[j];
+    __syncthreads();
     float inv[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        s[j] = fmaxf(s[j], 1e-4f) / 448.0f;
+        float m = red[0][cgi * 8 + j];
+#pragma unroll
+        for (int g = 1; g < kPcRowGroups; ++g) m = fmaxf(m, red[g][cgi * 8 + j]);
+        s[j] = fmaxf(m, 1e-4f) / 448.0f;
         inv[j] = 1.0f / s[j];
     }
-    if (blockIdx.y == 0) {
+    if (!active) return;
+    if (blockIdx.y == 0 && rg == 0) {
         *reinterpret_cast<float4*>(scales + col) = make_float4(s[0], s[1], s[2], s[3]);
         *reinterpret_cast<float4*>(scales + col + 4) = make_float4(s[4], s[5], s[6], s[7]);
     }
-    const int64_t r0 = static_cast<int64_t>(blockIdx.y) * kPcRowsPerBlock;
-    const int64_t r1 = r0 + kPcRowsPerBlock < rows ? r0 + kPcRowsPerBlock : rows;
-    for (int64_t r = r0; r < r1; ++r) {
+    const int rows_per_group = kPcRowsPerBlock / kPcRowGroups;   // 8
+    const int64_t r0 = static_cast<int64_t>(blockIdx.y) * kPcRowsPerBlock + rg * rows_per_group;
+    tk::u32x4 w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        w[i] = tk::u32x4{0u, 0u, 0u, 0u};
+        if (i < rows_per_group && r0 + i < rows) w[i] = tk::load_stream(x + static_cast<size_t>(r0 + i) * cols + col);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if (i >= rows_per_group || r0 + i >= rows) break;
         float v[8];
-        unpack8(tk::load_stream(x + static_cast<size_t>(r) * cols + col), v);
+        unpack8(w[i], v);
         uint2 o;
         o.x = tk::pack_fp8x4(tk::fp8_quotient(v[0], s[0], inv[0]), tk::fp8_quotient(v[1], s[1], inv[1]),
                              tk::fp8_quotient(v[2], s[2], inv[2]), tk::fp8_quotient(v[3], s[3], inv[3]));
         o.y = tk::pack_fp8x4(tk::fp8_quotient(v[4], s[4], inv[4]), tk::fp8_quotient(v[5], s[5], inv[5]),
                              tk::fp8_quotient(v[6], s[6], inv[6]), tk::fp8_quotient(v[7], s[7], inv[7]));
-        *reinterpret_cast<uint2*>(q + static_cast<size_t>(r) * cols + col) = o;
+        *reinterpret_cast<uint2*>(q + static_cast<size_t>(r0 + i) * cols + col) = o;
     }
 }
 
 // ------------------------------------------------------------------- FP4
-// E2M1 code of v (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6): the number of
-// midpoints below |v|, with a tie going to the even code, saturating at 6.
+// E2M1 code of v (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), nearest with ties to
+// the even code, saturating at 6, sign kept.  |v| is clamped to 6 and rounded
+// to one mantissa bit in fp32 by integer arithmetic (add 2^21 - 1 plus the
+// kept bit, drop 22 bits: round half to even); the code is then read off the
+// exponent and the kept bit.  Below 1 (the format's subnormal 0.5 step) the
+// value is first shifted by +1.0, which is exact here because the inputs carry
+// at most 8 significant bits, so [0, 1) rounds on the same half-unit grid.
 __device__ __forceinline__ uint32_t e2m1_code(float v)
 {
-    const float a = fabsf(v);
-    const uint32_t c = static_cast<uint32_t>(a > 0.25f) + static_cast<uint32_t>(a >= 0.75f) +
-                       static_cast<uint32_t>(a > 1.25f) + static_cast<uint32_t>(a >= 1.75f) +
-                       static_cast<uint32_t>(a > 2.5f) + static_cast<uint32_t>(a >= 3.5f) +
-                       static_cast<uint32_t>(a > 5.0f);
+    const float a = fminf(fabsf(v), 6.0f);
+    const bool sub = a < 1.0f;
+    uint32_t b = __float_as_uint(sub ? a + 1.0f : a);
+    b += 0x1FFFFFu + ((b >> 22) & 1u);
+    const uint32_t c = (b >> 22) - (sub ? 254u : 252u);
     return c | ((__float_as_uint(v) >> 28) & 8u);
 }
 
@@ -230,29 +283,34 @@ __global__ __launch_bounds__(tk::kBlock) void quant_fp4_kernel(
                       tk::uniform(threadIdx.x / tk::kWave);
     if (u >= rows * chunks) return;
     const int64_t r = u / chunks;
-    const int col = static_cast<int>(u - r * chunks) * 512 + lane * 8;
-    const bool active = col < cols;   // cols % 32 == 0: 4-lane groups wholly in or out
-    tk::u32x4 w = tk::u32x4{0u, 0u, 0u, 0u};
-    if (active) w = tk::load_stream(x + static_cast<size_t>(r) * cols + col);
-    float v[8];
-    unpack8(w, v);
+    const int col = static_cast<int>(u - r * chunks) * 2048 + lane * 32;   // one block per lane
+    if (col >= cols) return;                                               // cols % 32 == 0
+    const uint16_t* src = x + static_cast<size_t>(r) * cols + col;
+    tk::u32x4 w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = tk::load_stream(src + 8 * i);
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) unpack8(w[i], v + 8 * i);
     float amax = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    amax = fmaxf(amax, tk::dpp_f32<tk::kQuadXor1>(amax));
-    amax = fmaxf(amax, tk::dpp_f32<tk::kQuadXor2>(amax));   // one 32-column block per quad
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
     amax = fmaxf(amax, 1e-4f);
     int e;
     __builtin_frexpf(amax, &e);
     const float scale = __builtin_ldexpf(1.0f, e - 3);     // 2^(floor(log2 amax) - 2)
     const float inv = __builtin_ldexpf(1.0f, 3 - e);       // exact
-    uint32_t packed = 0;
+    uint32_t packed[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) packed |= e2m1_code(v[i] * inv) << (4 * i);
-    if (active) {
-        *reinterpret_cast<uint32_t*>(q + static_cast<size_t>(r) * (cols / 2) + col / 2) = packed;
-        if ((lane & 3) == 0) scales[static_cast<size_t>(r) * (cols / 32) + col / 32] = scale;
+    for (int i = 0; i < 4; ++i) {
+        uint32_t p = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) p |= e2m1_code(v[8 * i + j] * inv) << (4 * j);
+        packed[i] = p;
     }
+    tk::store_stream(q + static_cast<size_t>(r) * (cols / 2) + col / 2,
+                     tk::u32x4{packed[0], packed[1], packed[2], packed[3]});
+    scales[static_cast<size_t>(r) * (cols / 32) + col / 32] = scale;
 }
 
 unsigned blocks_for(int64_t waves) { return static_cast<unsigned>((waves + tk::kWavesPerBlock - 1) / tk::kWavesPerBlock); }
@@ -311,7 +369,7 @@ TK_EXPORT tk_status tk_quant(const void* x_bf16, int64_t rows, int32_t cols, int
         const int64_t n_blocks = (rows + kPcRowsPerBlock - 1) / kPcRowsPerBlock;
         if (n_chunks > 65535 || n_blocks > 65535)
             return fail(TK_ERR_UNSUPPORTED, "tk_quant: too many rows for per-channel");
-        const unsigned gx = static_cast<unsigned>((cols / 8 + tk::kBlock - 1) / tk::kBlock);
+        const unsigned gx = static_cast<unsigned>((cols + kPcCols - 1) / kPcCols);
         auto* partial = static_cast<float*>(workspace);
         e = tk::launch(quant_pc_partial_kernel, dim3(gx, static_cast<unsigned>(n_chunks)), block, 0,
                        stream, x, rows, cols, partial);
@@ -319,7 +377,7 @@ TK_EXPORT tk_status tk_quant(const void* x_bf16, int64_t rows, int32_t cols, int
         e = tk::launch(quant_pc_apply_kernel, dim3(gx, static_cast<unsigned>(n_blocks)), block, 0,
                        stream, x, rows, cols, static_cast<int>(n_chunks), partial, q, scales);
     } else {
-        const int chunks = (cols + 511) / 512;
+        const int chunks = (cols + 2047) / 2048;
         e = tk::launch(quant_fp4_kernel, dim3(blocks_for(rows * chunks)), block, 0, stream, x, rows,
                        cols, chunks, q, scales);
     }
