@@ -106,9 +106,22 @@ __global__ __launch_bounds__(kFinalThreads) void balance_final_kernel(
         float v = 0.f;
         int32_t c = 0;
         const int a = part * per, b = min(n_tiles, a + per);
-        for (int tl = a; tl < b; ++tl) {
-            v += part_p[static_cast<size_t>(tl) * E + e];
-            c += part_c[static_cast<size_t>(tl) * E + e];
+        for (int t0 = a; t0 < b; t0 += 8) {   // eight tiles' loads in flight, summed in order
+            float pv[8];
+            int32_t cv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const bool in = t0 + i < b;
+                pv[i] = in ? part_p[static_cast<size_t>(t0 + i) * E + e] : 0.f;
+                cv[i] = in ? part_c[static_cast<size_t>(t0 + i) * E + e] : 0;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (t0 + i < b) {
+                    v += pv[i];
+                    c += cv[i];
+                }
+            }
         }
         sp[part][e] = v;
         sc[part][e] = c;
