@@ -88,6 +88,8 @@ def _declare(L: ctypes.CDLL) -> ctypes.CDLL:
     L.orc_swiglu_quant.restype = i32
     L.orc_swiglu_f32.argtypes = [vp, i64, i32, vp, vp]
     L.orc_swiglu_f32.restype = i32
+    L.orc_swiglu_quant_t.argtypes = [vp, i64, i32, vp, vp, vp]
+    L.orc_swiglu_quant_t.restype = i32
     for name in ("orc_e4m3_from_f32_n", "orc_bf16_from_f32_n", "orc_bf16_from_f64_n",
                  "orc_sigmoid_f32_n", "orc_exp_f32_n"):
         getattr(L, name).argtypes = [vp, i64, vp]
@@ -309,6 +311,18 @@ def swiglu_f32(h, I: int, row_w=None):
     if lib().orc_swiglu_f32(_p(h), rows, I, _p(rw), _p(a)) != 0:
         raise ValueError("oracle swiglu: unsupported arguments")
     return a
+
+
+def swiglu_quant_t(h, I: int, row_w=None):
+    """Transposed output: a^T (I, rows) with 1x128 blocks along its rows."""
+    h = _c(h, np.uint16)
+    rows = h.shape[0]
+    q = np.empty((I, rows), np.uint8)
+    sc = np.empty((I, rows // 128), np.float32)
+    rw = None if row_w is None else _c(row_w, np.float32)
+    if lib().orc_swiglu_quant_t(_p(h), rows, I, _p(rw), _p(q), _p(sc)) != 0:
+        raise ValueError("oracle swiglu_quant_t: unsupported arguments")
+    return q, sc
 
 
 def swiglu_quant(h, I: int, row_w=None):

@@ -635,6 +635,29 @@ int orc_swiglu_f32(const uint16_t* h, int64_t rows, int I, const float* row_w, f
     return 0;
 }
 
+/* The transposed half of the SwiGLU + FP8 + transpose fusion: the same      */
+/* activations a (rows, I) quantised along the other axis, i.e. a^T (I, rows)*/
+/* with 1x128 blocks along its rows (128 consecutive tokens of one channel):*/
+/*   out_t[c, r] = E4M3(RN32(a[r, c] / scale_t[c, r/128])),                  */
+/*   scale_t[c, b] = RN32(max(max_{r in block b} |a[r, c]|, 1e-4) / 448).    */
+/* rows must be a multiple of 128.  out_t (I, rows), scales_t (I, rows/128).  */
+int orc_swiglu_quant_t(const uint16_t* h, int64_t rows, int I, const float* row_w,
+                       uint8_t* out_t, float* scales_t)
+{
+    if (rows < 0 || rows % 128 != 0 || I < 1) return -1;
+    float* a = (float*)malloc(sizeof(float) * (size_t)rows * (size_t)I);
+    float* col = (float*)malloc(sizeof(float) * (size_t)(rows > 0 ? rows : 1));
+    if (!a || !col) { free(a); free(col); return -1; }
+    orc_swiglu_f32(h, rows, I, row_w, a);
+    for (int c = 0; c < I; ++c) {
+        for (int64_t r = 0; r < rows; ++r) col[r] = a[(size_t)r * I + c];
+        orc_quant_f32_row(col, (int)rows, out_t + (size_t)c * rows, scales_t + (size_t)c * (rows / 128));
+    }
+    free(a); free(col);
+    return 0;
+}
+
+
 /* ------------------------------------------------------------------------ */
 /* Other granularities of the quantisation codec (TileKernels' quant/ module */
 /* lists per-token, per-block and per-channel FP8 and FP4).  Inputs are bf16 */

@@ -137,3 +137,28 @@ def test_row_weights_inverse_of_pos():
         t = row_src[r]
         j = int(np.nonzero(pos[t] == r)[0][0])
         assert rw[r] == w[t, j]
+
+
+@pytest.mark.parametrize("weighted", [False, True])
+def test_swiglu_quant_transposed_is_the_codec_along_columns(weighted):
+    """The transposed output against torch: the fp64 activations' columns in
+    blocks of 128 rows, torch fp32 amax/448 of the oracle's fp32 activations
+    and torch's float8 cast of the fp32 quotient; and the block-scale bound."""
+    rng = np.random.default_rng(75 + weighted)
+    R, I = 256, 384
+    h = _rows(rng, R, I, scale=3.0)
+    rw = rng.uniform(0.05, 2.5, R).astype(np.float32) if weighted else None
+    qt, st = oracle.swiglu_quant_t(h, I, rw)
+    a = torch.from_numpy(oracle.swiglu_f32(h, I, rw))               # (R, I) fp32
+    at = a.t().contiguous().view(I, R // 128, 128)
+    amax = at.abs().amax(2).clamp_min(torch.tensor(1e-4, dtype=torch.float32))
+    s_ref = amax / torch.tensor(448.0, dtype=torch.float32)
+    assert np.array_equal(st, s_ref.numpy())
+    q_ref = (at / s_ref[:, :, None]).to(torch.float8_e4m3fn).view(torch.uint8).reshape(I, R)
+    assert np.array_equal(qt, q_ref.numpy())
+    a64 = _torch_silu_mul64(h, I, rw).T                              # fp64, (I, R)
+    scr = np.repeat(st.astype(np.float64), 128, axis=1)
+    deq = oracle.e4m3_to_f64(qt) * scr
+    bound = np.maximum(np.abs(a64) * 2.0 ** -4, scr * 2.0 ** -10) * (1 + 2.0 ** -20) \
+        + 8 * 2.0 ** -24 * np.abs(a64)
+    assert np.all(np.abs(a64 - deq) <= bound)
