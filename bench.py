@@ -145,8 +145,22 @@ def bench_swiglu(tk, torch, y, n_rows, row_src, pos, w, steps):
     us = a.elapsed_time(b) * 1e3 / steps
     nbytes = R * 2 * I * 2 + R * I + R * (I // 128) * 4 + R * 4 + T * K * 8
     ops = R * I * SWIGLU_OPS_PER_ELEM
+    # the transposing form: both layouts from one read of h
+    qt = torch.empty((I, R), dtype=torch.uint8, device=y.device)
+    st = torch.empty((I, R // 128), dtype=torch.float32, device=y.device)
+    us_t = _time_calls(torch, lambda: tk.tk_swiglu_quant_t(h, row_src, pos, w, q, s, qt, st),
+                       min(steps, 20), (q, s, qt, st))
+    nbytes_t = nbytes + R * I + I * (R // 128) * 4
+    transposed = {"workload": f"as above, plus a^T ({I}, {R}) in 1x128 blocks along tokens",
+                  "us_per_call": round(us_t, 2), "timing": "HIP graph of the calls",
+                  "hbm_gbps": round(nbytes_t / us_t / 1e3, 1), "algorithmic_bytes": nbytes_t,
+                  "roofline": {"kernel": "swiglu_quant_t_kernel<true>", "bound": "alu",
+                               "achieved": round(ops / us_t / 1e6, 2),
+                               "peak": round(PEAK_VALU_TOPS, 2), "unit": "Top/s",
+                               "frac": round(ops / us_t / 1e6 / PEAK_VALU_TOPS, 4)}}
     return {"workload": f"{R} expanded rows of the step's routing, I={I} (gate|up bf16 -> "
                         "E4M3 + fp32 1x128 scales), routing weights applied",
+            "transposed": transposed,
             "us_per_launch": round(us, 2), "hbm_gbps": round(nbytes / us / 1e3, 1),
             "algorithmic_bytes": nbytes,
             "roofline": {"kernel": "swiglu_quant_kernel<true>", "bound": "alu",

@@ -245,6 +245,31 @@ tk_status tk_expand_quant(const void* x_bf16, int32_t T, int32_t H, int32_t k,
 tk_status tk_reduce(const void* y_bf16, int64_t rows, const int32_t* pos, const float* topk_w,
                     int32_t T, int32_t k, int32_t H, void* out_bf16, hipStream_t stream);
 
+/*
+ * tk_swiglu_quant_t -- the transposing form of the same fusion (SwiGLU + FP8
+ * quantisation + matrix transpose in one pass, "刚刚！DeepSeek开源高性能GPU算子库
+ * TileKernels", item quant/): from one read of h it writes both
+ *   out, scales      exactly as tk_swiglu_quant (1x128 blocks along each row)
+ *   out_t, scales_t  the transpose a^T (I, rows) quantised with 1x128 blocks
+ *                    along its rows -- 128 consecutive rows of one column of a:
+ *                    scales_t[c, b] = RN32(max(max |a[128b..128b+127, c]|,
+ *                    1e-4) / 448), out_t[c, r] = E4M3(RN32(a[r, c] /
+ *                    scales_t[c, r/128]))
+ * for all `rows` rows (a host count; no device-side row count).
+ *
+ * h_bf16        device, bf16 (rows, 2*I), 16-byte aligned
+ * rows          a multiple of 128, >= 0
+ * I             a positive multiple of 128
+ * row_src, pos, topk_w, T, k   as for tk_swiglu_quant (all NULL: unweighted)
+ * out           device, E4M3 (rows, I); scales: fp32 (rows, I/128)
+ * out_t         device, E4M3 (I, rows); scales_t: fp32 (I, rows/128)
+ *               (out and out_t 16-byte aligned)
+ */
+tk_status tk_swiglu_quant_t(const void* h_bf16, int64_t rows, int32_t I, const int32_t* row_src,
+                            const int32_t* pos, const float* topk_w, int32_t T, int32_t k,
+                            void* out, float* scales, void* out_t, float* scales_t,
+                            hipStream_t stream);
+
 /* --------------------------------------------- quantisation granularities */
 #define TK_QUANT_FP8_1X128 0        /* per-token 1x128 blocks, scale = amax/448 */
 #define TK_QUANT_FP8_1X128_POW2 1   /* 1x128 blocks, power-of-two scales */

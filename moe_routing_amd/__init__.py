@@ -13,6 +13,7 @@ step of the path runs in the library's HIP kernels; there is no fallback.
     tk_reduce(y, pos, topk_w)                  -> out
     tk_expert_standin(xq, scales, n_rows, mult) -> y
     tk_swiglu_quant(h, I, n_rows, row_src, pos, topk_w) -> (out, scales)
+    tk_swiglu_quant_t(h, row_src, pos, topk_w) -> (out, scales, out_t, scales_t)
     tk_balance_loss(logits, topk_idx, score)   -> (f, P, loss)
     tk_quant(x, mode)                          -> (codes, scales)
 """
@@ -94,6 +95,8 @@ def library() -> ctypes.CDLL:
         L.tk_expert_standin.restype = i32
         L.tk_swiglu_quant.argtypes = [vp, i64, vp, i32, vp, vp, vp, i32, i32, vp, vp, vp]
         L.tk_swiglu_quant.restype = i32
+        L.tk_swiglu_quant_t.argtypes = [vp, i64, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp]
+        L.tk_swiglu_quant_t.restype = i32
         L.tk_balance_workspace_bytes.argtypes = [i32, i32]
         L.tk_balance_workspace_bytes.restype = sz
         L.tk_balance_loss.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
@@ -342,3 +345,34 @@ def tk_quant(x: torch.Tensor, mode: int, out: torch.Tensor | None = None,
                                           0 if workspace is None else workspace.numel(),
                                           _stream(x)))
     return out, scales
+
+
+def tk_swiglu_quant_t(h: torch.Tensor, row_src: torch.Tensor | None = None,
+                      pos: torch.Tensor | None = None, topk_w: torch.Tensor | None = None,
+                      out=None, scales=None, out_t=None, scales_t=None):
+    """SwiGLU + 1x128 FP8 in both layouts: row-major (rows, I) and the
+    transpose (I, rows) with blocks along tokens.  rows % 128 == 0."""
+    _dev(h, "h", torch.bfloat16, 2)
+    rows, two_i = h.shape
+    I = two_i // 2
+    T = k = 0
+    if pos is not None:
+        _dev(pos, "pos", torch.int32, 2)
+        T, k = pos.shape
+    if row_src is not None:
+        _dev(row_src, "row_src", torch.int32)
+    if topk_w is not None:
+        _dev(topk_w, "topk_w", torch.float32)
+    dev = h.device
+    out = torch.empty((rows, I), dtype=torch.uint8, device=dev) if out is None else out
+    scales = torch.empty((rows, max(I // 128, 1)), dtype=torch.float32, device=dev) if scales is None else scales
+    out_t = torch.empty((I, rows), dtype=torch.uint8, device=dev) if out_t is None else out_t
+    scales_t = (torch.empty((I, max(rows // 128, 1)), dtype=torch.float32, device=dev)
+                if scales_t is None else scales_t)
+    for name, t, dt in (("out", out, torch.uint8), ("scales", scales, torch.float32),
+                        ("out_t", out_t, torch.uint8), ("scales_t", scales_t, torch.float32)):
+        _dev(t, name, dt)
+    _check("tk_swiglu_quant_t", library().tk_swiglu_quant_t(
+        _ptr(h), rows, I, _ptr(row_src), _ptr(pos), _ptr(topk_w), T, k, _ptr(out), _ptr(scales),
+        _ptr(out_t), _ptr(scales_t), _stream(h)))
+    return out, scales, out_t, scales_t

@@ -30,7 +30,8 @@ def lib():
     L = ctypes.CDLL(LIB)
     L.tk_last_error.restype = ctypes.c_char_p
     for name in ("tk_route", "tk_map", "tk_map_aligned", "tk_expand_quant", "tk_reduce",
-                 "tk_expert_standin", "tk_swiglu_quant", "tk_balance_loss", "tk_quant"):
+                 "tk_expert_standin", "tk_swiglu_quant", "tk_swiglu_quant_t", "tk_balance_loss",
+                 "tk_quant"):
         getattr(L, name).restype = ctypes.c_int32
     L.tk_map_workspace_bytes.restype = ctypes.c_size_t
     L.tk_balance_workspace_bytes.restype = ctypes.c_size_t
@@ -41,7 +42,7 @@ def lib():
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["tk_last_error", "tk_route", "tk_map_workspace_bytes", "tk_map",
                                   "tk_map_aligned", "tk_expand_quant", "tk_reduce",
-                                  "tk_expert_standin", "tk_swiglu_quant",
+                                  "tk_expert_standin", "tk_swiglu_quant", "tk_swiglu_quant_t",
                                   "tk_balance_workspace_bytes", "tk_balance_loss",
                                   "tk_quant_workspace_bytes", "tk_quant"])
 
@@ -256,3 +257,19 @@ def test_quant_rejects_bad_arguments(lib):
     f = lib.tk_quant_workspace_bytes
     assert f(I64(1000), I(256), I(3)) == 8 * 256 * 4      # 8 chunks of 128 rows
     assert f(I64(1000), I(256), I(0)) == 0
+
+
+def test_swiglu_t_rejects_bad_arguments(lib):
+    I32, I64 = ctypes.c_int32, ctypes.c_int64
+
+    def call(rows, I, rs=None, pos=None, w=None, T=0, k=0, h=FAKE, out=FAKE, out_t=FAKE):
+        return lib.tk_swiglu_quant_t(h, I64(rows), I32(I), rs, pos, w, I32(T), I32(k), out, FAKE,
+                                     out_t, FAKE, None)
+
+    assert call(100, 256) == ARG                  # rows % 128 != 0
+    assert call(-128, 256) == ARG
+    assert call(128, 200) == ARG
+    assert call(128, 256, rs=FAKE) == ARG
+    assert call(128, 256, h=None) == ARG
+    assert call(128, 256, out_t=MIS) == ARG
+    assert call(0, 256, h=None, out=None, out_t=None) == 0

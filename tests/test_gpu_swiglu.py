@@ -121,3 +121,54 @@ def test_swiglu_quant_v3_expert_shape_sampled():
     q_ref, s_ref = oracle.swiglu_quant(h_s, I, rw)
     assert np.array_equal(to_host(q.index_select(0, ridx)), q_ref)
     assert np.array_equal(to_host(s.index_select(0, ridx)), s_ref)
+
+
+# ------------------------------------------------------------- transposed --
+def _check_t(h, I, res, row_w=None):
+    out, sc, out_t, sc_t = (to_host(t) for t in res)
+    q_ref, s_ref = oracle.swiglu_quant(h, I, row_w)
+    qt_ref, st_ref = oracle.swiglu_quant_t(h, I, row_w)
+    assert np.array_equal(sc, s_ref) and np.array_equal(out, q_ref), "row-major output"
+    assert np.array_equal(sc_t, st_ref), "transposed scales"
+    bad = np.argwhere(out_t != qt_ref)
+    assert bad.size == 0, f"{len(bad)} transposed codes differ, first {bad[:4]}"
+
+
+@pytest.mark.parametrize("R,I", [(128, 128), (256, 384), (640, 2048), (128, 7168)])
+def test_swiglu_quant_t_random(R, I):
+    rng = np.random.default_rng(R * 3 + I)
+    h = _rows(rng, R, I)
+    res = tk.tk_swiglu_quant_t(to_dev(h, bf16=True))
+    torch.cuda.synchronize()
+    _check_t(h, I, res)
+
+
+def test_swiglu_quant_t_weighted_aligned_map():
+    """Rows laid out by the aligned map (segments padded to 128 rows), weights
+    through row_src / pos; padding rows have weight 0."""
+    rng = np.random.default_rng(83)
+    T, E, k, I = 400, 16, 4, 256
+    idx = synth.random_routing(rng, T, E, k)
+    _, offsets, pos, row_src = oracle.map_aligned(idx, E, 0, E, 128)
+    R = int(offsets[-1])
+    assert R % 128 == 0
+    w = rng.uniform(0.01, 1.0, (T, k)).astype(np.float32)
+    h = _rows(rng, R, I)
+    res = tk.tk_swiglu_quant_t(to_dev(h, bf16=True), to_dev(row_src), to_dev(pos), to_dev(w))
+    torch.cuda.synchronize()
+    _check_t(h, I, res, oracle.row_weights(pos, w, R))
+
+
+def test_swiglu_quant_t_corners():
+    rng = np.random.default_rng(84)
+    I, R = 256, 256
+    specials = np.array([0.0, -0.0, 20.0, -20.0, 100.0, -100.0, 1e-30, -3e-5, 1.0e30, 0.5],
+                        np.float32)
+    g = rng.choice(specials, (R, I)).astype(np.float32)
+    g[::3] = synth.normal_f32(rng, (len(g[::3]), I)) * np.float32(8.0)
+    u = synth.normal_f32(rng, (R, I))
+    u[:, 1::4] = 0.0                       # zero columns blocks in the transposed layout
+    h = synth.bf16_bits(np.concatenate([g, u], axis=1))
+    res = tk.tk_swiglu_quant_t(to_dev(h, bf16=True))
+    torch.cuda.synchronize()
+    _check_t(h, I, res)
