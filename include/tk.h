@@ -270,6 +270,19 @@ tk_status tk_swiglu_quant_t(const void* h_bf16, int64_t rows, int32_t I, const i
                             void* out, float* scales, void* out_t, float* scales_t,
                             hipStream_t stream);
 
+/*
+ * tk_silu_bf16 -- the gate factor of the fusion on its own: out[i] =
+ * RN32(g[i] * sigmoid(g[i])) with the pinned fp32 sigmoid, for bf16 g.  It
+ * runs the SwiGLU kernels' sigmoid lookup (the table the build tabulates
+ * from the pinned steps), so a caller can check that table on every bf16
+ * value or use the factor alone.
+ *
+ * g_bf16   device, bf16 (n), 2-byte aligned
+ * out      device, fp32 (n), 4-byte aligned
+ * n        >= 0 (0: nothing is launched)
+ */
+tk_status tk_silu_bf16(const void* g_bf16, int64_t n, float* out, hipStream_t stream);
+
 /* --------------------------------------------- quantisation granularities */
 #define TK_QUANT_FP8_1X128 0        /* per-token 1x128 blocks, scale = amax/448 */
 #define TK_QUANT_FP8_1X128_POW2 1   /* 1x128 blocks, power-of-two scales */

@@ -14,6 +14,7 @@ step of the path runs in the library's HIP kernels; there is no fallback.
     tk_expert_standin(xq, scales, n_rows, mult) -> y
     tk_swiglu_quant(h, I, n_rows, row_src, pos, topk_w) -> (out, scales)
     tk_swiglu_quant_t(h, row_src, pos, topk_w) -> (out, scales, out_t, scales_t)
+    tk_silu_bf16(g) -> fp32 RN(g * sigmoid(g))
     tk_balance_loss(logits, topk_idx, score)   -> (f, P, loss)
     tk_quant(x, mode)                          -> (codes, scales)
 """
@@ -97,6 +98,8 @@ def library() -> ctypes.CDLL:
         L.tk_swiglu_quant.restype = i32
         L.tk_swiglu_quant_t.argtypes = [vp, i64, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp]
         L.tk_swiglu_quant_t.restype = i32
+        L.tk_silu_bf16.argtypes = [vp, i64, vp, vp]
+        L.tk_silu_bf16.restype = i32
         L.tk_balance_workspace_bytes.argtypes = [i32, i32]
         L.tk_balance_workspace_bytes.restype = sz
         L.tk_balance_loss.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
@@ -376,3 +379,14 @@ def tk_swiglu_quant_t(h: torch.Tensor, row_src: torch.Tensor | None = None,
         _ptr(h), rows, I, _ptr(row_src), _ptr(pos), _ptr(topk_w), T, k, _ptr(out), _ptr(scales),
         _ptr(out_t), _ptr(scales_t), _stream(h)))
     return out, scales, out_t, scales_t
+
+
+def tk_silu_bf16(g: torch.Tensor, out=None):
+    """RN(g * sigmoid(g)) in fp32 for bf16 g (the SwiGLU kernels' sigmoid lookup)."""
+    _dev(g, "g", torch.bfloat16)
+    out = torch.empty(g.shape, dtype=torch.float32, device=g.device) if out is None else out
+    _dev(out, "out", torch.float32)
+    if out.numel() != g.numel():
+        raise ValueError("tk_silu_bf16: out must have g's number of elements")
+    _check("tk_silu_bf16", library().tk_silu_bf16(_ptr(g), g.numel(), _ptr(out), _stream(g)))
+    return out

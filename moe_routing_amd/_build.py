@@ -1,8 +1,11 @@
 """Build libtk.so (the HIP C-ABI library) in-tree for gfx950.
 
-Each .hip source is compiled to an object under _build/ in parallel, then
-linked into moe_routing_amd/libtk.so.  Always recompiles (a build check must
-compile); callers that only need the library load it when it exists.
+First a host-only generator (sigmoid_table_gen.hip) is compiled and run: it
+writes _build/sigmoid_table.inc, the pinned sigmoid at every bf16 value of
+its band, which swiglu.hip includes.  Then each .hip source is compiled to an
+object under _build/ in parallel and linked into moe_routing_amd/libtk.so.
+Always recompiles (a build check must compile); callers that only need the
+library load it when it exists.
 """
 from __future__ import annotations
 
@@ -30,8 +33,20 @@ FLAGS = [
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC,
+    "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC, "-I", BUILD,
 ]
+
+
+def _sigmoid_table() -> None:
+    exe = os.path.join(BUILD, "sigmoid_table_gen")
+    cmd = [HIPCC, "--cuda-host-only", "-O2", "-std=c++17", "-ffp-contract=off", "-I", INCLUDE,
+           "-I", CSRC, os.path.join(CSRC, "sigmoid_table_gen.hip"), "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on sigmoid_table_gen.hip:\n{r.stdout}\n{r.stderr}")
+    r = subprocess.run([exe, os.path.join(BUILD, "sigmoid_table.inc")], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sigmoid_table_gen failed:\n{r.stdout}\n{r.stderr}")
 
 
 def _compile(src: str) -> str:
@@ -45,6 +60,7 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
+    _sigmoid_table()
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"

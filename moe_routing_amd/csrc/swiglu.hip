@@ -14,34 +14,79 @@
 // then the 1x128 block codec of tk_expand_quant: amax = max(max |a|, 1e-4),
 // scale = RN(amax/448), q = E4M3(RN(a/scale)).
 //
-// Work unit = (row, 1024 output columns); one wave per unit, 4 waves per
-// workgroup.  Each lane owns 16 consecutive output columns: two 16-byte loads
-// of gate and two of up, one 16-byte store of codes, and lane 0 of each
-// 8-lane group (one 128-column block) stores the block's scale.  Inputs and
-// outputs are touched once: streaming loads and stores.  At ~45 VALU
-// instructions per element (the sigmoid's exp polynomial and IEEE division
-// dominate) this kernel is bound by vector ALU issue, not HBM.
+// The sigmoid is not evaluated per element: g is bf16, so s = sigmoid(g) is
+// one of a few thousand distinct fp32 values (outside a band of magnitudes it
+// is exactly 1/2, 1 or 0).  The build tabulates the pinned sigmoid over that
+// band (31 KB, sigmoid_table.h); every workgroup copies the table into LDS
+// once and reads s with one LDS load after a clamp and an index -- about
+// eight instructions where exp and an IEEE division took about thirty.  The
+// values are the pinned sigmoid's, bit for bit.
+//
+// One wave per row, in chunks of 1024 output columns.  The grid is persistent
+// (at most kSBlocks workgroups of 8 waves, so the table is copied about a
+// thousand times, not once per row); each wave strides over the rows.  In a
+// chunk each lane owns 16 consecutive output columns: two 16-byte loads of
+// gate and two of up, one 16-byte store of codes, and lane 0 of each 8-lane
+// group (one 128-column block) stores the block's scale.  Inputs and outputs
+// are touched once: streaming loads and stores.  With the sigmoid a lookup,
+// the kernel streams at about the rate of a device copy.
 //
 // The weight of row r is found from the map's outputs: t = row_src[r] and the
 // slot j with pos[t, j] == r give w_r = topk_w[t, j]; a row no slot points at
-// gets weight 0.
+// gets weight 0.  These are two dependent loads, so they are issued one or
+// two rows ahead of the row that needs them.
 //
 // tk_swiglu_quant_t adds the transpose of the fusion: the same activations
 // also quantised as a^T (I, rows) in 1x128 blocks along its rows (128 tokens
 // of one channel, the layout a weight-gradient GEMM reads), both outputs from
 // one pass over h.
+#include <algorithm>
+
+#include "sigmoid_table.h"
 #include "tk_internal.h"
 
 namespace {
 
 constexpr int kChunk = 1024;   // output columns per unit (16 per lane)
 
+// sigmoid of the bf16 values in the table's band, interleaved by sign; the
+// entries are written at build time by sigmoid_table_gen (same pinned steps)
+__device__ __align__(16) const float kSigmoidBf16[tk::kSigEntries] = {
+#include "sigmoid_table.inc"
+};
+static_assert(tk::kSigEntries % 4 == 0, "the table is copied in 16-byte pieces");
+
+// All THREADS threads of the workgroup copy the table into LDS (the caller
+// places the barrier).
+template <int THREADS>
+__device__ __forceinline__ void load_sigmoid_table(float* lds)
+{
+    const auto* src = reinterpret_cast<const tk::u32x4*>(kSigmoidBf16);
+    auto* dst = reinterpret_cast<tk::u32x4*>(lds);
+    for (int i = threadIdx.x; i < static_cast<int>(tk::kSigEntries / 4); i += THREADS) dst[i] = src[i];
+}
+
+// RN(g * sigmoid(g)) for the bf16 g with magnitude bits m (15 bits) and sign
+// bit sgn, read from the LDS table.
+__device__ __forceinline__ float silu_bf16(float g, uint32_t m, uint32_t sgn, const float* tab)
+{
+    const uint32_t c = m < tk::kSigLo - 1 ? tk::kSigLo - 1 : (m > tk::kSigHi ? tk::kSigHi : m);
+    return g * tab[((c - (tk::kSigLo - 1)) << 1) | sgn];
+}
+__device__ __forceinline__ float silu_lo(uint32_t w, const float* tab)
+{
+    return silu_bf16(tk::bf16_lo(w), w & 0x7FFFu, (w >> 15) & 1u, tab);
+}
+__device__ __forceinline__ float silu_hi(uint32_t w, const float* tab)
+{
+    return silu_bf16(tk::bf16_hi(w), (w >> 16) & 0x7FFFu, w >> 31, tab);
+}
+
 struct SwigluArgs {
     const uint16_t* h;
     int64_t cap;
     const int32_t* n_rows;
     int I;
-    int chunks;
     const int32_t* row_src;
     const int32_t* pos;
     const float* topk_w;
@@ -50,78 +95,137 @@ struct SwigluArgs {
     float* scales;
 };
 
-template <bool WEIGHTED>
-__global__ __launch_bounds__(tk::kBlock) void swiglu_quant_kernel(SwigluArgs a)
+// The weight of expanded row r: its token t = row_src[r], and the slot j of t
+// with pos[t, j] == r carries it (0 when t is out of range or no slot points
+// at r, e.g. a padding row).  Lane j < k holds slot j: one load of pos and one
+// of topk_w per lane, then a ballot picks the slot (a token's slots point at
+// distinct rows, so at most one lane matches).
+__device__ __forceinline__ float select_weight(int32_t p, float w, uint32_t r)
 {
+    const uint64_t hit = __ballot(p == static_cast<int32_t>(r));
+    if (hit == 0) return 0.0f;
+    const int j = tk::uniform(__ffsll(static_cast<long long>(hit)) - 1);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
+}
+__device__ __forceinline__ float pick_weight(const SwigluArgs& a, int t, int lane, uint32_t r)
+{
+    int32_t p = -1;
+    float w = 0.0f;
+    if (t >= 0 && t < a.T && lane < a.k) {
+        p = a.pos[static_cast<size_t>(t) * a.k + lane];
+        w = a.topk_w[static_cast<size_t>(t) * a.k + lane];
+    }
+    return select_weight(p, w, r);
+}
+
+constexpr int kSThreads = 512;                 // 8 waves per workgroup
+constexpr int kSWaves = kSThreads / tk::kWave;
+constexpr int kSBlocks = 1024;                 // 4 per CU of a 256-CU device
+
+template <bool WEIGHTED>
+__global__ __launch_bounds__(kSThreads) void swiglu_quant_kernel(SwigluArgs a)
+{
+    __shared__ __align__(16) float sig[tk::kSigEntries];
+    load_sigmoid_table<kSThreads>(sig);
+    __syncthreads();
+
     const int lane = threadIdx.x & (tk::kWave - 1);
-    const int64_t u = static_cast<int64_t>(blockIdx.x) * tk::kWavesPerBlock +
-                      tk::uniform(threadIdx.x / tk::kWave);
-    int64_t rows = a.cap;
+    int64_t rows64 = a.cap;
     if (a.n_rows != nullptr) {
         const int64_t n = *a.n_rows;
-        rows = n < 0 ? 0 : (n < a.cap ? n : a.cap);
+        rows64 = n < 0 ? 0 : (n < a.cap ? n : a.cap);
     }
-    if (u >= rows * a.chunks) return;
-    const int64_t r = u / a.chunks;
-    const int col0 = static_cast<int>(u - r * a.chunks) * kChunk;
-    const int col = col0 + lane * 16;
-    const bool active = col < a.I;   // I % 128 == 0: 8-lane groups are wholly in or out
+    // the host bounds rows_capacity below 2^31 / 8: 32-bit row indices, and
+    // r + 2 * stride does not wrap
+    const uint32_t rows = static_cast<uint32_t>(rows64);
+    const uint32_t stride = gridDim.x * kSWaves;
+    uint32_t r = blockIdx.x * kSWaves + tk::uniform(threadIdx.x / tk::kWave);
 
-    const uint16_t* hr = a.h + static_cast<size_t>(r) * 2 * a.I;
-    tk::u32x4 g0 = tk::u32x4{0u, 0u, 0u, 0u}, g1 = g0, u0 = g0, u1 = g0;
-    if (active) {
-        g0 = tk::load_stream(hr + col);
-        g1 = tk::load_stream(hr + col + 8);
-        u0 = tk::load_stream(hr + a.I + col);
-        u1 = tk::load_stream(hr + a.I + col + 8);
-    }
-    // the row weight's three dependent loads overlap the row's loads above
+    // Routing weights run ahead of the rows: while row r is processed, the
+    // token of row r + 2*stride and the slots of row r + stride's token are
+    // in flight, so their dependent loads never wait in line.
     float w = 1.0f;
+    int t1 = -1;
     if constexpr (WEIGHTED) {
-        w = 0.0f;
-        const int t = a.row_src[r];
-        if (t >= 0 && t < a.T) {
-            const int32_t* p = a.pos + static_cast<size_t>(t) * a.k;
-            for (int j = 0; j < a.k; ++j)
-                if (p[j] == r) w = a.topk_w[static_cast<size_t>(t) * a.k + j];
-        }
+        const int t0 = r < rows ? a.row_src[r] : -1;
+        w = pick_weight(a, t0, lane, r);
+        t1 = r + stride < rows ? a.row_src[r + stride] : -1;
     }
-
-    const uint32_t gw[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-    const uint32_t uw[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-    float v[16];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float ga = tk::bf16_lo(gw[i]), gb = tk::bf16_hi(gw[i]);
-        const float ua = tk::bf16_lo(uw[i]), ub = tk::bf16_hi(uw[i]);
-        float va = (ga * tk::pinned_sigmoid(ga)) * ua;
-        float vb = (gb * tk::pinned_sigmoid(gb)) * ub;
+    for (; r < rows; r += stride) {
+        int t2 = -1;
+        int32_t p1 = -1;
+        float w1 = 0.0f;
         if constexpr (WEIGHTED) {
-            va = va * w;
-            vb = vb * w;
+            if (r + 2 * stride < rows) t2 = a.row_src[r + 2 * stride];
+            if (t1 >= 0 && t1 < a.T && lane < a.k) {
+                p1 = a.pos[static_cast<size_t>(t1) * a.k + lane];
+                w1 = a.topk_w[static_cast<size_t>(t1) * a.k + lane];
+            }
         }
-        v[2 * i] = va;
-        v[2 * i + 1] = vb;
-    }
-    float amax = 0.f;
+        const uint16_t* hr = a.h + static_cast<size_t>(r) * 2 * a.I;
+        uint8_t* orow = a.out + static_cast<size_t>(r) * a.I;
+        float* srow = a.scales + static_cast<size_t>(r) * (a.I / 128);
+        for (int col0 = 0; col0 < a.I; col0 += kChunk) {
+            const int col = col0 + lane * 16;
+            const bool active = col < a.I;   // I % 128 == 0: 8-lane groups are wholly in or out
+            tk::u32x4 g0 = tk::u32x4{0u, 0u, 0u, 0u}, g1 = g0, u0 = g0, u1 = g0;
+            if (active) {
+                g0 = tk::load_stream(hr + col);
+                g1 = tk::load_stream(hr + col + 8);
+                u0 = tk::load_stream(hr + a.I + col);
+                u1 = tk::load_stream(hr + a.I + col + 8);
+            }
+            const uint32_t gw[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+            const uint32_t uw[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+            float v[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    amax = fmaxf(tk::max_run8(amax), 1e-4f);   // one 128-column block per 8 lanes
-    const float scale = amax / 448.0f;
-    const float inv = 1.0f / scale;
-    tk::u32x4 q;
-    q.x = tk::pack_fp8x4(tk::fp8_quotient(v[0], scale, inv), tk::fp8_quotient(v[1], scale, inv),
-                         tk::fp8_quotient(v[2], scale, inv), tk::fp8_quotient(v[3], scale, inv));
-    q.y = tk::pack_fp8x4(tk::fp8_quotient(v[4], scale, inv), tk::fp8_quotient(v[5], scale, inv),
-                         tk::fp8_quotient(v[6], scale, inv), tk::fp8_quotient(v[7], scale, inv));
-    q.z = tk::pack_fp8x4(tk::fp8_quotient(v[8], scale, inv), tk::fp8_quotient(v[9], scale, inv),
-                         tk::fp8_quotient(v[10], scale, inv), tk::fp8_quotient(v[11], scale, inv));
-    q.w = tk::pack_fp8x4(tk::fp8_quotient(v[12], scale, inv), tk::fp8_quotient(v[13], scale, inv),
-                         tk::fp8_quotient(v[14], scale, inv), tk::fp8_quotient(v[15], scale, inv));
-    if (active) {
-        tk::store_stream(a.out + static_cast<size_t>(r) * a.I + col, q);
-        if ((lane & 7) == 0) a.scales[static_cast<size_t>(r) * (a.I / 128) + col / 128] = scale;
+            for (int i = 0; i < 8; ++i) {
+                float va = silu_lo(gw[i], sig) * tk::bf16_lo(uw[i]);
+                float vb = silu_hi(gw[i], sig) * tk::bf16_hi(uw[i]);
+                if constexpr (WEIGHTED) {
+                    va = va * w;
+                    vb = vb * w;
+                }
+                v[2 * i] = va;
+                v[2 * i + 1] = vb;
+            }
+            float amax = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+            amax = fmaxf(tk::max_run8(amax), 1e-4f);   // one 128-column block per 8 lanes
+            const float scale = amax / 448.0f;
+            const float inv = 1.0f / scale;
+            tk::u32x4 q;
+            q.x = tk::pack_fp8x4(tk::fp8_quotient(v[0], scale, inv), tk::fp8_quotient(v[1], scale, inv),
+                                 tk::fp8_quotient(v[2], scale, inv), tk::fp8_quotient(v[3], scale, inv));
+            q.y = tk::pack_fp8x4(tk::fp8_quotient(v[4], scale, inv), tk::fp8_quotient(v[5], scale, inv),
+                                 tk::fp8_quotient(v[6], scale, inv), tk::fp8_quotient(v[7], scale, inv));
+            q.z = tk::pack_fp8x4(tk::fp8_quotient(v[8], scale, inv), tk::fp8_quotient(v[9], scale, inv),
+                                 tk::fp8_quotient(v[10], scale, inv), tk::fp8_quotient(v[11], scale, inv));
+            q.w = tk::pack_fp8x4(tk::fp8_quotient(v[12], scale, inv), tk::fp8_quotient(v[13], scale, inv),
+                                 tk::fp8_quotient(v[14], scale, inv), tk::fp8_quotient(v[15], scale, inv));
+            if (active) {
+                tk::store_stream(orow + col, q);
+                if ((lane & 7) == 0) srow[col / 128] = scale;
+            }
+        }
+        if constexpr (WEIGHTED) {
+            w = select_weight(p1, w1, r + stride);
+            t1 = t2;
+        }
     }
+}
+
+// RN(g * sigmoid(g)) elementwise for n bf16 values (the SwiGLU gate factor).
+__global__ __launch_bounds__(tk::kBlock) void silu_kernel(const uint16_t* __restrict__ g, int64_t n,
+                                                          float* __restrict__ out)
+{
+    __shared__ __align__(16) float sig[tk::kSigEntries];
+    load_sigmoid_table<tk::kBlock>(sig);
+    __syncthreads();
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * tk::kBlock;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * tk::kBlock + threadIdx.x; i < n; i += stride)
+        out[i] = silu_lo(g[i], sig);
 }
 
 // ---------------------------------------------------------------- transposed
@@ -130,134 +234,192 @@ __global__ __launch_bounds__(tk::kBlock) void swiglu_quant_kernel(SwigluArgs a)
 // with 1x128 blocks along each row (the tile's 128 columns), and the
 // transpose a^T with 1x128 blocks along each of its rows (the tile's 128 rows
 // of one column).  Thread (rg, cg) = (tid / 16, tid % 16) holds rows 4*rg..
-// and columns 8*cg.. of the tile (32 values, so the kernel keeps enough waves
-// resident to hide its ALU latency): a row's 128 columns live in 16
-// consecutive lanes (DPP row max), a column's 128 rows in 32 row groups
-// across the eight waves (LDS max).  The transposed codes are staged in LDS
-// and leave as whole 16-byte pieces of out_t's rows.
+// and columns 8*cg.. of the tile (32 values, few enough registers for six
+// waves per SIMD): a row's 128 columns live in 16 consecutive lanes (DPP row
+// max), a column's 128 rows in 32 row groups across the eight waves (LDS
+// max).  The transposed codes are staged in LDS and leave as whole 16-byte
+// pieces of out_t's rows.  The grid is persistent (at most kTBlocks
+// workgroups, each striding over the tiles), so the sigmoid table is copied
+// once per workgroup.
 constexpr int kTile = 128;
 constexpr int kTThreads = 512;
 constexpr int kTRows = 4;                         // rows per thread
 constexpr int kTGroups = kTile / kTRows;          // 32 row groups
 constexpr int kTPitch = kTile + 16;               // bytes per staged out_t row (padded)
 
+constexpr int kTBlocks = 768;                     // 3 per CU of a 256-CU device
+
+// (6 waves per SIMD is what the LDS allows: three workgroups per CU; the
+// register budget is held to it)
 template <bool WEIGHTED>
-__global__ __launch_bounds__(kTThreads) void swiglu_quant_t_kernel(SwigluArgs a, uint8_t* __restrict__ out_t,
-                                                                 float* __restrict__ scales_t)
+__global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(6)))
+void swiglu_quant_t_kernel(SwigluArgs a, int64_t tiles, uint8_t* __restrict__ out_t,
+                           float* __restrict__ scales_t)
 {
+    __shared__ __align__(16) float sig[tk::kSigEntries];
     __shared__ float w_row[kTile];
-    __shared__ float col_part[kTGroups][kTile];
     __shared__ float col_scale[kTile];
-    __shared__ uint8_t codes_t[kTile * kTPitch];
+    // the column partial maxima, then (once they are reduced) the staged codes
+    __shared__ __align__(16) uint8_t stage[kTile * kTPitch];
+    static_assert(sizeof(float) * kTGroups * kTile <= kTile * kTPitch, "stage too small");
+    auto col_part = reinterpret_cast<float (*)[kTile]>(stage);
+    load_sigmoid_table<kTThreads>(sig);
+
     const int tiles_c = a.I / kTile;
-    const int64_t tr = blockIdx.x / tiles_c;
-    const int tc = static_cast<int>(blockIdx.x - tr * tiles_c);
-    const int64_t r0 = tr * kTile;
-    const int c0 = tc * kTile;
     const int rg = threadIdx.x >> 4, cg = threadIdx.x & 15;
     const int64_t R = a.cap;
 
-    // the tile's row loads first; the row weights' dependent loads overlap them
-    tk::u32x4 gw[kTRows], uw[kTRows];
-#pragma unroll
-    for (int i = 0; i < kTRows; ++i) {
-        const uint16_t* hr = a.h + static_cast<size_t>(r0 + rg * kTRows + i) * 2 * a.I;
-        gw[i] = tk::load_stream(hr + c0 + cg * 8);
-        uw[i] = tk::load_stream(hr + a.I + c0 + cg * 8);
+    // Routing weights run one tile ahead.  Four threads share a tile row
+    // (wrow = tid / 4): thread wsub loads slots wsub and wsub + 4 of the row's
+    // token in the middle of the previous tile and picks the weight at its
+    // end; slots from 8 on (k > 8) are read when the weight is picked.  The
+    // matching slot's weight bits are OR-ed across the quad (a token's slots
+    // point at distinct rows, so at most one thread matches; none leaves +0).
+    const int wrow = threadIdx.x >> 2, wsub = threadIdx.x & 3;
+    int32_t pa = -1, pb = -1;
+    float wa = 0.0f, wb = 0.0f;
+    auto load_slots = [&](int t) {
+        pa = pb = -1;
+        if (t >= 0 && t < a.T) {
+            const size_t base = static_cast<size_t>(t) * a.k;
+            if (wsub < a.k) {
+                pa = a.pos[base + wsub];
+                wa = a.topk_w[base + wsub];
+            }
+            if (wsub + 4 < a.k) {
+                pb = a.pos[base + wsub + 4];
+                wb = a.topk_w[base + wsub + 4];
+            }
+        }
+    };
+    auto pick_weight = [&](int t, int64_t row) {
+        const int32_t r = static_cast<int32_t>(row);
+        uint32_t bits = 0;
+        if (pa == r) bits = __float_as_uint(wa);
+        if (pb == r) bits = __float_as_uint(wb);
+        if (t >= 0 && t < a.T) {
+            for (int j = wsub + 8; j < a.k; j += 4) {
+                const size_t sl = static_cast<size_t>(t) * a.k + j;
+                if (a.pos[sl] == r) bits = __float_as_uint(a.topk_w[sl]);
+            }
+        }
+        bits |= tk::dpp_u32<tk::kQuadXor1>(bits);
+        bits |= tk::dpp_u32<tk::kQuadXor2>(bits);
+        if (wsub == 0) w_row[wrow] = __uint_as_float(bits);
+    };
+    if constexpr (WEIGHTED) {
+        if (blockIdx.x < tiles) {
+            const int64_t row = blockIdx.x / tiles_c * kTile + wrow;
+            const int t = a.row_src[row];
+            load_slots(t);
+            pick_weight(t, row);
+        }
     }
-    if (threadIdx.x < kTile) {
-        float w = 1.0f;
+    __syncthreads();   // the table and the first tile's weights
+
+    for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+        const int64_t tr = tile / tiles_c;
+        const int tc = static_cast<int>(tile - tr * tiles_c);
+        const int64_t r0 = tr * kTile;
+        const int c0 = tc * kTile;
+        const int64_t next = tile + gridDim.x;
+        const int64_t next_row = next / tiles_c * kTile + wrow;
+
+        tk::u32x4 gw[kTRows], uw[kTRows];
+#pragma unroll
+        for (int i = 0; i < kTRows; ++i) {
+            const uint16_t* hr = a.h + static_cast<size_t>(r0 + rg * kTRows + i) * 2 * a.I;
+            gw[i] = tk::load_stream(hr + c0 + cg * 8);
+            uw[i] = tk::load_stream(hr + a.I + c0 + cg * 8);
+        }
+        int tok_next = -1;
         if constexpr (WEIGHTED) {
-            const int64_t r = r0 + threadIdx.x;
-            w = 0.0f;
-            const int t = a.row_src[r];
-            if (t >= 0 && t < a.T) {
-                const int32_t* p = a.pos + static_cast<size_t>(t) * a.k;
-                for (int j = 0; j < a.k; ++j)
-                    if (p[j] == r) w = a.topk_w[static_cast<size_t>(t) * a.k + j];
+            if (next < tiles) tok_next = a.row_src[next_row];
+        }
+
+        float v[kTRows][8];
+#pragma unroll
+        for (int i = 0; i < kTRows; ++i) {
+            const uint32_t g4[4] = {gw[i].x, gw[i].y, gw[i].z, gw[i].w};
+            const uint32_t u4[4] = {uw[i].x, uw[i].y, uw[i].z, uw[i].w};
+            const float w = WEIGHTED ? w_row[rg * kTRows + i] : 1.0f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float va = silu_lo(g4[j], sig) * tk::bf16_lo(u4[j]);
+                float vb = silu_hi(g4[j], sig) * tk::bf16_hi(u4[j]);
+                if constexpr (WEIGHTED) {
+                    va = va * w;
+                    vb = vb * w;
+                }
+                v[i][2 * j] = va;
+                v[i][2 * j + 1] = vb;
             }
         }
-        w_row[threadIdx.x] = w;
-    }
-    __syncthreads();
 
-    float v[kTRows][8];
+        // column partial maxima first (the LDS round trip overlaps the row codes)
 #pragma unroll
-    for (int i = 0; i < kTRows; ++i) {
-        const uint32_t g4[4] = {gw[i].x, gw[i].y, gw[i].z, gw[i].w};
-        const uint32_t u4[4] = {uw[i].x, uw[i].y, uw[i].z, uw[i].w};
-        const float w = w_row[rg * kTRows + i];
+        for (int j = 0; j < 8; ++j) {
+            float m = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float ga = tk::bf16_lo(g4[j]), gb = tk::bf16_hi(g4[j]);
-            const float ua = tk::bf16_lo(u4[j]), ub = tk::bf16_hi(u4[j]);
-            float va = (ga * tk::pinned_sigmoid(ga)) * ua;
-            float vb = (gb * tk::pinned_sigmoid(gb)) * ub;
-            if constexpr (WEIGHTED) {
-                va = va * w;
-                vb = vb * w;
-            }
-            v[i][2 * j] = va;
-            v[i][2 * j + 1] = vb;
+            for (int i = 0; i < kTRows; ++i) m = fmaxf(m, fabsf(v[i][j]));
+            col_part[rg][cg * 8 + j] = m;
         }
-    }
 
-    // column partial maxima first (the LDS round trip overlaps the row codes)
+        // row-major codes: one 1x128 block per tile row
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        float m = 0.f;
+        for (int i = 0; i < kTRows; ++i) {
+            float m = 0.f;
 #pragma unroll
-        for (int i = 0; i < kTRows; ++i) m = fmaxf(m, fabsf(v[i][j]));
-        col_part[rg][cg * 8 + j] = m;
-    }
+            for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[i][j]));
+            m = fmaxf(m, tk::dpp_f32<tk::kQuadXor1>(m));
+            m = fmaxf(m, tk::dpp_f32<tk::kQuadXor2>(m));
+            m = fmaxf(m, tk::dpp_f32<tk::kHalfMirror>(m));
+            m = fmaxf(m, tk::dpp_f32<tk::kMirror>(m));      // the 16 lanes of this row group
+            const float scale = fmaxf(m, 1e-4f) / 448.0f;
+            const float inv = 1.0f / scale;
+            uint2 o;
+            o.x = tk::pack_fp8x4(tk::fp8_quotient(v[i][0], scale, inv), tk::fp8_quotient(v[i][1], scale, inv),
+                                 tk::fp8_quotient(v[i][2], scale, inv), tk::fp8_quotient(v[i][3], scale, inv));
+            o.y = tk::pack_fp8x4(tk::fp8_quotient(v[i][4], scale, inv), tk::fp8_quotient(v[i][5], scale, inv),
+                                 tk::fp8_quotient(v[i][6], scale, inv), tk::fp8_quotient(v[i][7], scale, inv));
+            const int64_t r = r0 + rg * kTRows + i;
+            *reinterpret_cast<uint2*>(a.out + static_cast<size_t>(r) * a.I + c0 + cg * 8) = o;
+            if (cg == 0) a.scales[static_cast<size_t>(r) * (a.I / 128) + tc] = scale;
+        }
+        if constexpr (WEIGHTED) load_slots(tok_next);   // the next tile's slots
 
-    // row-major codes: one 1x128 block per tile row
+        // transposed codes: one 1x128 block per tile column
+        __syncthreads();   // col_part complete; w_row read out
+        if (threadIdx.x < kTile) {
+            float m = col_part[0][threadIdx.x];
 #pragma unroll
-    for (int i = 0; i < kTRows; ++i) {
-        float m = 0.f;
+            for (int g = 1; g < kTGroups; ++g) m = fmaxf(m, col_part[g][threadIdx.x]);
+            const float scale = fmaxf(m, 1e-4f) / 448.0f;
+            col_scale[threadIdx.x] = scale;
+            scales_t[static_cast<size_t>(c0 + threadIdx.x) * (R / kTile) + tr] = scale;
+        }
+        __syncthreads();   // col_scale ready, col_part consumed: stage now holds codes
 #pragma unroll
-        for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[i][j]));
-        m = fmaxf(m, tk::dpp_f32<tk::kQuadXor1>(m));
-        m = fmaxf(m, tk::dpp_f32<tk::kQuadXor2>(m));
-        m = fmaxf(m, tk::dpp_f32<tk::kHalfMirror>(m));
-        m = fmaxf(m, tk::dpp_f32<tk::kMirror>(m));      // the 16 lanes of this row group
-        const float scale = fmaxf(m, 1e-4f) / 448.0f;
-        const float inv = 1.0f / scale;
-        uint2 o;
-        o.x = tk::pack_fp8x4(tk::fp8_quotient(v[i][0], scale, inv), tk::fp8_quotient(v[i][1], scale, inv),
-                             tk::fp8_quotient(v[i][2], scale, inv), tk::fp8_quotient(v[i][3], scale, inv));
-        o.y = tk::pack_fp8x4(tk::fp8_quotient(v[i][4], scale, inv), tk::fp8_quotient(v[i][5], scale, inv),
-                             tk::fp8_quotient(v[i][6], scale, inv), tk::fp8_quotient(v[i][7], scale, inv));
-        const int64_t r = r0 + rg * kTRows + i;
-        *reinterpret_cast<uint2*>(a.out + static_cast<size_t>(r) * a.I + c0 + cg * 8) = o;
-        if (cg == 0) a.scales[static_cast<size_t>(r) * (a.I / 128) + tc] = scale;
-    }
-
-    // transposed codes: one 1x128 block per tile column
-    __syncthreads();
-    if (threadIdx.x < kTile) {
-        float m = col_part[0][threadIdx.x];
-#pragma unroll
-        for (int g = 1; g < kTGroups; ++g) m = fmaxf(m, col_part[g][threadIdx.x]);
-        const float scale = fmaxf(m, 1e-4f) / 448.0f;
-        col_scale[threadIdx.x] = scale;
-        scales_t[static_cast<size_t>(c0 + threadIdx.x) * (R / kTile) + tr] = scale;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const float scale = col_scale[cg * 8 + j];
-        const float inv = 1.0f / scale;
-        const uint32_t q = tk::pack_fp8x4(tk::fp8_quotient(v[0][j], scale, inv), tk::fp8_quotient(v[1][j], scale, inv),
-                                          tk::fp8_quotient(v[2][j], scale, inv), tk::fp8_quotient(v[3][j], scale, inv));
-        *reinterpret_cast<uint32_t*>(codes_t + (cg * 8 + j) * kTPitch + rg * kTRows) = q;
-    }
-    __syncthreads();
-    // 128 out_t rows of 128 bytes: 8 threads per row, 16 bytes each
-    for (int i = threadIdx.x; i < kTile * 8; i += kTThreads) {
-        const int c = i >> 3, part = i & 7;
-        const tk::u32x4 q = *reinterpret_cast<const tk::u32x4*>(codes_t + c * kTPitch + part * 16);
-        tk::store_stream(out_t + static_cast<size_t>(c0 + c) * R + r0 + part * 16, q);
+        for (int j = 0; j < 8; ++j) {
+            const float scale = col_scale[cg * 8 + j];
+            const float inv = 1.0f / scale;
+            const uint32_t q = tk::pack_fp8x4(tk::fp8_quotient(v[0][j], scale, inv),
+                                              tk::fp8_quotient(v[1][j], scale, inv),
+                                              tk::fp8_quotient(v[2][j], scale, inv),
+                                              tk::fp8_quotient(v[3][j], scale, inv));
+            *reinterpret_cast<uint32_t*>(stage + (cg * 8 + j) * kTPitch + rg * kTRows) = q;
+        }
+        __syncthreads();
+        // 128 out_t rows of 128 bytes: 8 threads per row, 16 bytes each
+        for (int i = threadIdx.x; i < kTile * 8; i += kTThreads) {
+            const int c = i >> 3, part = i & 7;
+            const tk::u32x4 q = *reinterpret_cast<const tk::u32x4*>(stage + c * kTPitch + part * 16);
+            tk::store_stream(out_t + static_cast<size_t>(c0 + c) * R + r0 + part * 16, q);
+        }
+        if constexpr (WEIGHTED) {
+            if (next < tiles) pick_weight(tok_next, next_row);
+        }
+        __syncthreads();   // stage read out before the next tile; its weights published
     }
 }
 
@@ -285,13 +447,11 @@ TK_EXPORT tk_status tk_swiglu_quant(const void* h_bf16, int64_t rows_capacity,
         (n_rows && !tk::aligned4(n_rows)) || (row_src && !tk::aligned4(row_src)) ||
         (pos && !tk::aligned4(pos)) || (topk_w && !tk::aligned4(topk_w)))
         return fail(TK_ERR_ARG, "tk_swiglu_quant: h/out must be 16-byte aligned, the rest 4-byte");
-    const int chunks = (I + kChunk - 1) / kChunk;
-    const int64_t units = rows_capacity * chunks;
-    const int64_t blocks = (units + tk::kWavesPerBlock - 1) / tk::kWavesPerBlock;
-    if (blocks > INT32_MAX) return fail(TK_ERR_UNSUPPORTED, "tk_swiglu_quant: too many rows");
-    const SwigluArgs args{static_cast<const uint16_t*>(h_bf16), rows_capacity, n_rows, I, chunks,
+    if (rows_capacity > INT32_MAX / 8) return fail(TK_ERR_UNSUPPORTED, "tk_swiglu_quant: too many rows");
+    const int64_t blocks = std::min<int64_t>((rows_capacity + kSWaves - 1) / kSWaves, kSBlocks);
+    const SwigluArgs args{static_cast<const uint16_t*>(h_bf16), rows_capacity, n_rows, I,
                           row_src, pos, topk_w, T, k, static_cast<uint8_t*>(out), scales};
-    const dim3 grid(static_cast<unsigned>(blocks)), block(tk::kBlock);
+    const dim3 grid(static_cast<unsigned>(blocks)), block(kSThreads);
     const hipError_t e = weighted
         ? tk::launch(swiglu_quant_kernel<true>, grid, block, 0, stream, args)
         : tk::launch(swiglu_quant_kernel<false>, grid, block, 0, stream, args);
@@ -325,13 +485,26 @@ TK_EXPORT tk_status tk_swiglu_quant_t(const void* h_bf16, int64_t rows, int32_t 
         (pos && !tk::aligned4(pos)) || (topk_w && !tk::aligned4(topk_w)))
         return fail(TK_ERR_ARG, "tk_swiglu_quant_t: h/out/out_t must be 16-byte aligned, the rest 4-byte");
     const int64_t tiles = rows / kTile * (I / kTile);
-    if (tiles > INT32_MAX) return fail(TK_ERR_UNSUPPORTED, "tk_swiglu_quant_t: too many rows");
-    const SwigluArgs args{static_cast<const uint16_t*>(h_bf16), rows, nullptr, I, 0,
+    const SwigluArgs args{static_cast<const uint16_t*>(h_bf16), rows, nullptr, I,
                           row_src, pos, topk_w, T, k, static_cast<uint8_t*>(out), scales};
-    const dim3 grid(static_cast<unsigned>(tiles)), block(kTThreads);
+    const dim3 grid(static_cast<unsigned>(std::min<int64_t>(tiles, kTBlocks))), block(kTThreads);
     auto* ot = static_cast<uint8_t*>(out_t);
     const hipError_t e = weighted
-        ? tk::launch(swiglu_quant_t_kernel<true>, grid, block, 0, stream, args, ot, scales_t)
-        : tk::launch(swiglu_quant_t_kernel<false>, grid, block, 0, stream, args, ot, scales_t);
+        ? tk::launch(swiglu_quant_t_kernel<true>, grid, block, 0, stream, args, tiles, ot, scales_t)
+        : tk::launch(swiglu_quant_t_kernel<false>, grid, block, 0, stream, args, tiles, ot, scales_t);
     return tk::launched(e, "tk_swiglu_quant_t");
+}
+
+TK_EXPORT tk_status tk_silu_bf16(const void* g_bf16, int64_t n, float* out, hipStream_t stream)
+{
+    using tk::fail;
+    if (n < 0) return fail(TK_ERR_ARG, "tk_silu_bf16: n < 0");
+    if (n == 0) return tk::ok();
+    if (g_bf16 == nullptr || out == nullptr) return fail(TK_ERR_ARG, "tk_silu_bf16: NULL pointer");
+    if (reinterpret_cast<uintptr_t>(g_bf16) % 2 != 0 || !tk::aligned4(out))
+        return fail(TK_ERR_ARG, "tk_silu_bf16: g must be 2-byte and out 4-byte aligned");
+    const int64_t blocks = std::min<int64_t>((n + tk::kBlock - 1) / tk::kBlock, 1024);
+    const hipError_t e = tk::launch(silu_kernel, dim3(static_cast<unsigned>(blocks)), dim3(tk::kBlock), 0,
+                                    stream, static_cast<const uint16_t*>(g_bf16), n, out);
+    return tk::launched(e, "tk_silu_bf16");
 }

@@ -166,13 +166,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 // multiply-adds.  Every step is one IEEE fp32 operation (the library is built
 // with -ffp-contract=off), so the result is the same on any IEEE machine
 // that follows these steps; y is cut to [-86, 88] so p * 2^n stays normal.
+// (Host and device: the build evaluates it on the host for the bf16 sigmoid
+// table the SwiGLU kernels read.)
 constexpr float kLog2e = 0x1.715476p+0f;    // RN(log2 e)
 constexpr float kLn2Hi = 0x1.62e4p-1f;      // ln 2 truncated to 16 bits
 constexpr float kLn2Lo = 0x1.7f7d1cp-20f;   // RN(ln 2 - kLn2Hi)
 constexpr float kC2 = 0x1p-1f, kC3 = 0x1.555556p-3f, kC4 = 0x1.555556p-5f,
                 kC5 = 0x1.111112p-7f, kC6 = 0x1.6c16c2p-10f, kC7 = 0x1.a01a02p-13f;  // RN(1/i!)
 
-__device__ __forceinline__ float pinned_exp(float y)
+__host__ __device__ __forceinline__ float pinned_exp(float y)
 {
     if (y > 88.0f) return __builtin_inff();
     if (y < -86.0f) return 0.0f;
@@ -190,7 +192,7 @@ __device__ __forceinline__ float pinned_exp(float y)
     return __builtin_ldexpf(p, static_cast<int>(n));
 }
 
-__device__ __forceinline__ float pinned_sigmoid(float x) { return 1.0f / (1.0f + pinned_exp(-x)); }
+__host__ __device__ __forceinline__ float pinned_sigmoid(float x) { return 1.0f / (1.0f + pinned_exp(-x)); }
 
 // -------------------------------------------------- 1x128 E4M3 codec
 // x / scale for scale > 0 by Markstein's correction on the correctly rounded

@@ -30,7 +30,8 @@ def lib():
     L = ctypes.CDLL(LIB)
     L.tk_last_error.restype = ctypes.c_char_p
     for name in ("tk_route", "tk_map", "tk_map_aligned", "tk_expand_quant", "tk_reduce",
-                 "tk_expert_standin", "tk_swiglu_quant", "tk_swiglu_quant_t", "tk_balance_loss",
+                 "tk_expert_standin", "tk_swiglu_quant", "tk_swiglu_quant_t",
+                                  "tk_silu_bf16", "tk_balance_loss",
                  "tk_quant"):
         getattr(L, name).restype = ctypes.c_int32
     L.tk_map_workspace_bytes.restype = ctypes.c_size_t
@@ -43,6 +44,7 @@ def test_header_declares_the_entry_points():
     assert _declared() == sorted(["tk_last_error", "tk_route", "tk_map_workspace_bytes", "tk_map",
                                   "tk_map_aligned", "tk_expand_quant", "tk_reduce",
                                   "tk_expert_standin", "tk_swiglu_quant", "tk_swiglu_quant_t",
+                                  "tk_silu_bf16",
                                   "tk_balance_workspace_bytes", "tk_balance_loss",
                                   "tk_quant_workspace_bytes", "tk_quant"])
 
@@ -273,3 +275,14 @@ def test_swiglu_t_rejects_bad_arguments(lib):
     assert call(128, 256, h=None) == ARG
     assert call(128, 256, out_t=MIS) == ARG
     assert call(0, 256, h=None, out=None, out_t=None) == 0
+
+
+def test_silu_rejects_bad_arguments(lib):
+    f = lib.tk_silu_bf16
+    I64 = ctypes.c_int64
+    assert f(FAKE, I64(-1), FAKE, None) == ARG
+    assert f(None, I64(4), FAKE, None) == ARG
+    assert f(FAKE, I64(4), None, None) == ARG
+    assert f(FAKE, I64(4), MIS1, None) == ARG         # out not 4-byte aligned
+    assert f(MIS1, I64(4), FAKE, None) == ARG         # g not 2-byte aligned
+    assert f(None, I64(0), None, None) == 0

@@ -172,3 +172,39 @@ def test_swiglu_quant_t_corners():
     res = tk.tk_swiglu_quant_t(to_dev(h, bf16=True))
     torch.cuda.synchronize()
     _check_t(h, I, res)
+
+
+def test_swiglu_quant_t_many_tiles_weighted():
+    """More 128x128 tiles (50 x 16 = 800) than the kernel's persistent grid, so
+    workgroups take a second tile; weighted through a map of the rows."""
+    rng = np.random.default_rng(85)
+    R, I = 50 * 128, 2048
+    T, k = R // 4, 4
+    idx = synth.random_routing(rng, T, 64, k)
+    _, offsets, pos, row_src = oracle.map_routes(idx, 64)
+    assert int(offsets[-1]) == R
+    w = rng.uniform(0.01, 1.0, (T, k)).astype(np.float32)
+    h = _rows(rng, R, I)
+    res = tk.tk_swiglu_quant_t(to_dev(h, bf16=True), to_dev(row_src), to_dev(pos), to_dev(w))
+    torch.cuda.synchronize()
+    _check_t(h, I, res, oracle.row_weights(pos, w, R))
+
+
+# ------------------------------------------------------ sigmoid lookup --
+def test_silu_bf16_every_value():
+    """RN(g * sigmoid(g)) on all 65536 bf16 values (the SwiGLU kernels' table
+    lookup) against the oracle's pinned sigmoid: bit-exact, NaN where NaN."""
+    bits = np.arange(0x10000, dtype=np.uint32).astype(np.uint16)
+    got = to_host(tk.tk_silu_bf16(to_dev(bits, bf16=True)))
+    g = (bits.astype(np.uint32) << 16).view(np.float32)
+    with np.errstate(invalid="ignore"):
+        ref = (g * oracle.sigmoid_f32(g)).astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    bad = np.nonzero(got[~nan].view(np.uint32) != ref[~nan].view(np.uint32))[0]
+    assert bad.size == 0, f"{bad.size} values differ, first bf16 bits {bits[~nan][bad[:4]]}"
+    # and a strided, odd-length call through the grid-stride loop
+    many = np.resize(bits, 3 * 65536 + 7)
+    got2 = to_host(tk.tk_silu_bf16(to_dev(many, bf16=True)))
+    assert np.array_equal(got2.view(np.uint32)[~np.isnan(got2)],
+                          np.resize(got, many.size).view(np.uint32)[~np.isnan(got2)])
