@@ -14,8 +14,10 @@
 //                            nibble), 1x32 blocks, scale 2^(floor(log2 amax)-2)
 //
 // Kernels:
-//  - 1x128 (and pow2): one wave per (row, 1024 columns), 16 columns per lane,
-//    a 128-column block per 8 lanes (amax by a 3-step DPP butterfly).
+//  - 1x128 (and pow2): the matrix as one flat run of values (no block
+//    straddles a row); one wave per 2048 values, 8 per lane and piece (16-byte
+//    loads, 1 KB contiguous per wave instruction), a 128-value block per 16
+//    lanes (amax by a 4-step DPP butterfly), 8 bytes of codes per lane.
 //  - 128x128: one 256-thread workgroup per tile; each thread holds an 8x8
 //    patch (eight 16-byte row loads), the tile amax is a DPP wave max then an
 //    LDS step over the four waves.
@@ -24,9 +26,11 @@
 //    flight, row groups combined in LDS) into the workspace; pass 2 takes
 //    the maximum over the chunks (exact in any order), forms the scales and
 //    quantises 64 rows per workgroup.
-//  - FP4: one wave per (row, 2048 columns), one 32-column block per lane
-//    (four 16-byte loads, one 16-byte store of codes); E2M1 encoding by
-//    integer rounding of the fp32 bits to one mantissa bit (ties to even).
+//  - FP4: the matrix as one flat run of values (no block straddles a row);
+//    one wave per 2048 values, one 32-value block per lane quad (16-byte
+//    loads, the wave reading 1 KB contiguous per instruction; one 32-bit
+//    word of codes per lane); E2M1 encoding by integer rounding of the fp32
+//    bits to one mantissa bit (ties to even).
 // Codes are written with streaming stores; the E4M3 quotient is the shared
 // Markstein-corrected one, exact for power-of-two scales.
 #include "tk_internal.h"
@@ -44,21 +48,6 @@ __device__ __forceinline__ float pow2_scale_e4m3(float amax)
     return __builtin_ldexpf(1.0f, m <= 0.875f ? x - 9 : x - 8);
 }
 
-__device__ __forceinline__ tk::u32x4 quant16_e4m3(const float (&v)[16], float scale)
-{
-    const float inv = 1.0f / scale;
-    tk::u32x4 q;
-    q.x = tk::pack_fp8x4(tk::fp8_quotient(v[0], scale, inv), tk::fp8_quotient(v[1], scale, inv),
-                         tk::fp8_quotient(v[2], scale, inv), tk::fp8_quotient(v[3], scale, inv));
-    q.y = tk::pack_fp8x4(tk::fp8_quotient(v[4], scale, inv), tk::fp8_quotient(v[5], scale, inv),
-                         tk::fp8_quotient(v[6], scale, inv), tk::fp8_quotient(v[7], scale, inv));
-    q.z = tk::pack_fp8x4(tk::fp8_quotient(v[8], scale, inv), tk::fp8_quotient(v[9], scale, inv),
-                         tk::fp8_quotient(v[10], scale, inv), tk::fp8_quotient(v[11], scale, inv));
-    q.w = tk::pack_fp8x4(tk::fp8_quotient(v[12], scale, inv), tk::fp8_quotient(v[13], scale, inv),
-                         tk::fp8_quotient(v[14], scale, inv), tk::fp8_quotient(v[15], scale, inv));
-    return q;
-}
-
 // eight bf16 (one 16-byte word) -> fp32
 __device__ __forceinline__ void unpack8(tk::u32x4 w, float* v)
 {
@@ -71,35 +60,52 @@ __device__ __forceinline__ void unpack8(tk::u32x4 w, float* v)
 }
 
 // ------------------------------------------------------------------ 1x128
+// The matrix as one flat run of rows * cols values (cols % 128 == 0, so no
+// block straddles a row; a block's codes sit at flat and its scale at
+// flat / 128).  A wave takes 2048 consecutive values in four 512-value
+// pieces; in each piece lane l holds values 8l..8l+7 (one 16-byte load, the
+// wave reading 1 KB contiguous), 16 lanes make a 128-value block (DPP max),
+// and each lane stores its 8 codes as one 8-byte word.
+constexpr int kQPerWave = 2048;
+
 template <bool POW2>
 __global__ __launch_bounds__(tk::kBlock) void quant_1x128_kernel(
-    const uint16_t* __restrict__ x, int64_t rows, int cols, int chunks, uint8_t* __restrict__ q,
-    float* __restrict__ scales)
+    const uint16_t* __restrict__ x, int64_t n, uint8_t* __restrict__ q, float* __restrict__ scales)
 {
     const int lane = threadIdx.x & (tk::kWave - 1);
-    const int64_t u = static_cast<int64_t>(blockIdx.x) * tk::kWavesPerBlock +
-                      tk::uniform(threadIdx.x / tk::kWave);
-    if (u >= rows * chunks) return;
-    const int64_t r = u / chunks;
-    const int col = static_cast<int>(u - r * chunks) * 1024 + lane * 16;
-    const bool active = col < cols;
-    tk::u32x4 a = tk::u32x4{0u, 0u, 0u, 0u}, b = a;
-    if (active) {
-        a = tk::load_stream(x + static_cast<size_t>(r) * cols + col);
-        b = tk::load_stream(x + static_cast<size_t>(r) * cols + col + 8);
-    }
-    float v[16];
-    unpack8(a, v);
-    unpack8(b, v + 8);
-    float amax = 0.f;
+    const int64_t base = (static_cast<int64_t>(blockIdx.x) * tk::kWavesPerBlock +
+                          tk::uniform(threadIdx.x / tk::kWave)) * kQPerWave;
+    if (base >= n) return;
+    tk::u32x4 w[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    amax = tk::max_run8(amax);
-    const float scale = POW2 ? pow2_scale_e4m3(amax) : fmaxf(amax, 1e-4f) / 448.0f;
-    const tk::u32x4 code = quant16_e4m3(v, scale);
-    if (active) {
-        tk::store_stream(q + static_cast<size_t>(r) * cols + col, code);
-        if ((lane & 7) == 0) scales[static_cast<size_t>(r) * (cols / 128) + col / 128] = scale;
+    for (int j = 0; j < 4; ++j) {
+        const int64_t f = base + j * 512 + lane * 8;
+        w[j] = f < n ? tk::load_stream(x + f) : tk::u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t f = base + j * 512 + lane * 8;   // n % 128 == 0: 16-lane runs wholly in or out
+        float v[8];
+        unpack8(w[j], v);
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+        amax = fmaxf(amax, tk::dpp_f32<tk::kQuadXor1>(amax));
+        amax = fmaxf(amax, tk::dpp_f32<tk::kQuadXor2>(amax));
+        amax = fmaxf(amax, tk::dpp_f32<tk::kHalfMirror>(amax));
+        amax = fmaxf(amax, tk::dpp_f32<tk::kMirror>(amax));
+        const float scale = POW2 ? pow2_scale_e4m3(amax) : fmaxf(amax, 1e-4f) / 448.0f;
+        const float inv = 1.0f / scale;
+        uint2 c;
+        c.x = tk::pack_fp8x4(tk::fp8_quotient(v[0], scale, inv), tk::fp8_quotient(v[1], scale, inv),
+                             tk::fp8_quotient(v[2], scale, inv), tk::fp8_quotient(v[3], scale, inv));
+        c.y = tk::pack_fp8x4(tk::fp8_quotient(v[4], scale, inv), tk::fp8_quotient(v[5], scale, inv),
+                             tk::fp8_quotient(v[6], scale, inv), tk::fp8_quotient(v[7], scale, inv));
+        if (f < n) {
+            __builtin_nontemporal_store(c.x, reinterpret_cast<uint32_t*>(q + f));
+            __builtin_nontemporal_store(c.y, reinterpret_cast<uint32_t*>(q + f + 4));
+            if ((lane & 15) == 0) scales[f / 128] = scale;
+        }
     }
 }
 
@@ -274,43 +280,51 @@ __device__ __forceinline__ uint32_t e2m1_code(float v)
     return c | ((__float_as_uint(v) >> 28) & 8u);
 }
 
+// The matrix is taken as one flat run of rows * cols values: cols % 32 == 0,
+// so no block straddles a row, and a block's codes and scale sit at flat / 2
+// and flat / 32 of the row-major outputs.  A wave takes 2048 consecutive
+// values in four 512-value pieces; in each piece lane l holds values
+// 8l..8l+7 (one 16-byte load, the wave reading 1 KB contiguous), a lane quad
+// is one 32-value block (DPP max), and each lane stores its 8 codes as one
+// 32-bit word.
+constexpr int kFp4PerWave = 2048;
+
 __global__ __launch_bounds__(tk::kBlock) void quant_fp4_kernel(
-    const uint16_t* __restrict__ x, int64_t rows, int cols, int chunks, uint8_t* __restrict__ q,
-    float* __restrict__ scales)
+    const uint16_t* __restrict__ x, int64_t n, uint8_t* __restrict__ q, float* __restrict__ scales)
 {
     const int lane = threadIdx.x & (tk::kWave - 1);
-    const int64_t u = static_cast<int64_t>(blockIdx.x) * tk::kWavesPerBlock +
-                      tk::uniform(threadIdx.x / tk::kWave);
-    if (u >= rows * chunks) return;
-    const int64_t r = u / chunks;
-    const int col = static_cast<int>(u - r * chunks) * 2048 + lane * 32;   // one block per lane
-    if (col >= cols) return;                                               // cols % 32 == 0
-    const uint16_t* src = x + static_cast<size_t>(r) * cols + col;
+    const int64_t base = (static_cast<int64_t>(blockIdx.x) * tk::kWavesPerBlock +
+                          tk::uniform(threadIdx.x / tk::kWave)) * kFp4PerWave;
+    if (base >= n) return;
     tk::u32x4 w[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = tk::load_stream(src + 8 * i);
-    float v[32];
+    for (int j = 0; j < 4; ++j) {
+        const int64_t f = base + j * 512 + lane * 8;
+        w[j] = f < n ? tk::load_stream(x + f) : tk::u32x4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) unpack8(w[i], v + 8 * i);
-    float amax = 0.f;
+    for (int j = 0; j < 4; ++j) {
+        const int64_t f = base + j * 512 + lane * 8;   // n % 32 == 0: quads are wholly in or out
+        float v[8];
+        unpack8(w[j], v);
+        float amax = 0.f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    amax = fmaxf(amax, 1e-4f);
-    int e;
-    __builtin_frexpf(amax, &e);
-    const float scale = __builtin_ldexpf(1.0f, e - 3);     // 2^(floor(log2 amax) - 2)
-    const float inv = __builtin_ldexpf(1.0f, 3 - e);       // exact
-    uint32_t packed[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+        amax = fmaxf(amax, tk::dpp_f32<tk::kQuadXor1>(amax));
+        amax = fmaxf(amax, tk::dpp_f32<tk::kQuadXor2>(amax));
+        amax = fmaxf(amax, 1e-4f);
+        int e;
+        __builtin_frexpf(amax, &e);
+        const float scale = __builtin_ldexpf(1.0f, e - 3);     // 2^(floor(log2 amax) - 2)
+        const float inv = __builtin_ldexpf(1.0f, 3 - e);       // exact
         uint32_t p = 0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) p |= e2m1_code(v[8 * i + j] * inv) << (4 * j);
-        packed[i] = p;
+        for (int i = 0; i < 8; ++i) p |= e2m1_code(v[i] * inv) << (4 * i);
+        if (f < n) {
+            __builtin_nontemporal_store(p, reinterpret_cast<uint32_t*>(q + f / 2));
+            if ((lane & 3) == 0) scales[f / 32] = scale;
+        }
     }
-    tk::store_stream(q + static_cast<size_t>(r) * (cols / 2) + col / 2,
-                     tk::u32x4{packed[0], packed[1], packed[2], packed[3]});
-    scales[static_cast<size_t>(r) * (cols / 32) + col / 32] = scale;
 }
 
 unsigned blocks_for(int64_t waves) { return static_cast<unsigned>((waves + tk::kWavesPerBlock - 1) / tk::kWavesPerBlock); }
@@ -350,11 +364,14 @@ TK_EXPORT tk_status tk_quant(const void* x_bf16, int64_t rows, int32_t cols, int
     const dim3 block(tk::kBlock);
     hipError_t e = hipSuccess;
     if (mode == TK_QUANT_FP8_1X128 || mode == TK_QUANT_FP8_1X128_POW2) {
-        const int chunks = (cols + 1023) / 1024;
-        const dim3 grid(blocks_for(rows * chunks));
+        const int64_t n = rows * cols;
+        const int64_t waves = (n + kQPerWave - 1) / kQPerWave;
+        if ((waves + tk::kWavesPerBlock - 1) / tk::kWavesPerBlock > INT32_MAX)
+            return fail(TK_ERR_UNSUPPORTED, "tk_quant: too many values");
+        const dim3 grid(blocks_for(waves));
         e = mode == TK_QUANT_FP8_1X128_POW2
-            ? tk::launch(quant_1x128_kernel<true>, grid, block, 0, stream, x, rows, cols, chunks, q, scales)
-            : tk::launch(quant_1x128_kernel<false>, grid, block, 0, stream, x, rows, cols, chunks, q, scales);
+            ? tk::launch(quant_1x128_kernel<true>, grid, block, 0, stream, x, n, q, scales)
+            : tk::launch(quant_1x128_kernel<false>, grid, block, 0, stream, x, n, q, scales);
     } else if (mode == TK_QUANT_FP8_128X128) {
         const int64_t tiles = (rows + 127) / 128 * (cols / 128);
         if (tiles > INT32_MAX) return fail(TK_ERR_UNSUPPORTED, "tk_quant: too many tiles");
@@ -377,9 +394,11 @@ TK_EXPORT tk_status tk_quant(const void* x_bf16, int64_t rows, int32_t cols, int
         e = tk::launch(quant_pc_apply_kernel, dim3(gx, static_cast<unsigned>(n_blocks)), block, 0,
                        stream, x, rows, cols, static_cast<int>(n_chunks), partial, q, scales);
     } else {
-        const int chunks = (cols + 2047) / 2048;
-        e = tk::launch(quant_fp4_kernel, dim3(blocks_for(rows * chunks)), block, 0, stream, x, rows,
-                       cols, chunks, q, scales);
+        const int64_t n = rows * cols;
+        const int64_t waves = (n + kFp4PerWave - 1) / kFp4PerWave;
+        if ((waves + tk::kWavesPerBlock - 1) / tk::kWavesPerBlock > INT32_MAX)
+            return fail(TK_ERR_UNSUPPORTED, "tk_quant: too many values for FP4");
+        e = tk::launch(quant_fp4_kernel, dim3(blocks_for(waves)), block, 0, stream, x, n, q, scales);
     }
     return tk::launched(e, "tk_quant");
 }
