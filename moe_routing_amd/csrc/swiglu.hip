@@ -66,21 +66,23 @@ __device__ __forceinline__ void load_sigmoid_table(float* lds)
     for (int i = threadIdx.x; i < static_cast<int>(tk::kSigEntries / 4); i += THREADS) dst[i] = src[i];
 }
 
-// RN(g * sigmoid(g)) for the bf16 g with magnitude bits m (15 bits) and sign
-// bit sgn, read from the LDS table.
-__device__ __forceinline__ float silu_bf16(float g, uint32_t m, uint32_t sgn, const float* tab)
+// sigmoid(g) for the bf16 g with magnitude bits m (15 bits) and sign bit sgn,
+// read from the LDS table; silu = RN(g * sigmoid(g)).
+__device__ __forceinline__ float sigmoid_bf16(uint32_t m, uint32_t sgn, const float* tab)
 {
     const uint32_t c = m < tk::kSigLo - 1 ? tk::kSigLo - 1 : (m > tk::kSigHi ? tk::kSigHi : m);
-    return g * tab[((c - (tk::kSigLo - 1)) << 1) | sgn];
+    return tab[((c - (tk::kSigLo - 1)) << 1) | sgn];
 }
-__device__ __forceinline__ float silu_lo(uint32_t w, const float* tab)
+__device__ __forceinline__ float sigmoid_lo(uint32_t w, const float* tab)
 {
-    return silu_bf16(tk::bf16_lo(w), w & 0x7FFFu, (w >> 15) & 1u, tab);
+    return sigmoid_bf16(w & 0x7FFFu, (w >> 15) & 1u, tab);
 }
-__device__ __forceinline__ float silu_hi(uint32_t w, const float* tab)
+__device__ __forceinline__ float sigmoid_hi(uint32_t w, const float* tab)
 {
-    return silu_bf16(tk::bf16_hi(w), (w >> 16) & 0x7FFFu, w >> 31, tab);
+    return sigmoid_bf16((w >> 16) & 0x7FFFu, w >> 31, tab);
 }
+__device__ __forceinline__ float silu_lo(uint32_t w, const float* tab) { return tk::bf16_lo(w) * sigmoid_lo(w, tab); }
+__device__ __forceinline__ float silu_hi(uint32_t w, const float* tab) { return tk::bf16_hi(w) * sigmoid_hi(w, tab); }
 
 struct SwigluArgs {
     const uint16_t* h;
@@ -246,6 +248,18 @@ constexpr int kTThreads = 512;
 constexpr int kTRows = 4;                         // rows per thread
 constexpr int kTGroups = kTile / kTRows;          // 32 row groups
 constexpr int kTPitch = kTile + 16;               // bytes per staged out_t row (padded)
+static_assert(kTRows == 4, "a row group's rows are handed out by quad broadcasts");
+// lane i of each lane quad, to all four lanes (DPP quad_perm [i,i,i,i]); i is
+// a compile-time constant after unrolling
+__device__ __forceinline__ float quad_lane(float x, int i)
+{
+    switch (i) {
+    case 0: return tk::dpp_f32<0x00>(x);
+    case 1: return tk::dpp_f32<0x55>(x);
+    case 2: return tk::dpp_f32<0xAA>(x);
+    default: return tk::dpp_f32<0xFF>(x);
+    }
+}
 
 constexpr int kTBlocks = 768;                     // 3 per CU of a 256-CU device
 
@@ -259,6 +273,7 @@ void swiglu_quant_t_kernel(SwigluArgs a, int64_t tiles, uint8_t* __restrict__ ou
     __shared__ __align__(16) float sig[tk::kSigEntries];
     __shared__ float w_row[kTile];
     __shared__ float col_scale[kTile];
+    __shared__ float col_inv[kTile];
     // the column partial maxima, then (once they are reduced) the staged codes
     __shared__ __align__(16) uint8_t stage[kTile * kTPitch];
     static_assert(sizeof(float) * kTGroups * kTile <= kTile * kTPitch, "stage too small");
@@ -271,8 +286,8 @@ void swiglu_quant_t_kernel(SwigluArgs a, int64_t tiles, uint8_t* __restrict__ ou
 
     // Routing weights run one tile ahead.  Four threads share a tile row
     // (wrow = tid / 4): thread wsub loads slots wsub and wsub + 4 of the row's
-    // token in the middle of the previous tile and picks the weight at its
-    // end; slots from 8 on (k > 8) are read when the weight is picked.  The
+    // token once the previous tile's codes are staged, and picks the weight
+    // after that tile's stores; slots from 8 on (k > 8) are read when the weight is picked.  The
     // matching slot's weight bits are OR-ed across the quad (a token's slots
     // point at distinct rows, so at most one thread matches; none leaves +0).
     const int wrow = threadIdx.x >> 2, wsub = threadIdx.x & 3;
@@ -342,11 +357,18 @@ void swiglu_quant_t_kernel(SwigluArgs a, int64_t tiles, uint8_t* __restrict__ ou
         for (int i = 0; i < kTRows; ++i) {
             const uint32_t g4[4] = {gw[i].x, gw[i].y, gw[i].z, gw[i].w};
             const uint32_t u4[4] = {uw[i].x, uw[i].y, uw[i].z, uw[i].w};
+            // the row's eight table reads go out together, then the arithmetic
+            float sg[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                sg[2 * j] = sigmoid_lo(g4[j], sig);
+                sg[2 * j + 1] = sigmoid_hi(g4[j], sig);
+            }
             const float w = WEIGHTED ? w_row[rg * kTRows + i] : 1.0f;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                float va = silu_lo(g4[j], sig) * tk::bf16_lo(u4[j]);
-                float vb = silu_hi(g4[j], sig) * tk::bf16_hi(u4[j]);
+                float va = (tk::bf16_lo(g4[j]) * sg[2 * j]) * tk::bf16_lo(u4[j]);
+                float vb = (tk::bf16_hi(g4[j]) * sg[2 * j + 1]) * tk::bf16_hi(u4[j]);
                 if constexpr (WEIGHTED) {
                     va = va * w;
                     vb = vb * w;
@@ -365,7 +387,11 @@ void swiglu_quant_t_kernel(SwigluArgs a, int64_t tiles, uint8_t* __restrict__ ou
             col_part[rg][cg * 8 + j] = m;
         }
 
-        // row-major codes: one 1x128 block per tile row
+        // row-major codes: one 1x128 block per tile row.  The row maxima are
+        // 16-lane DPP maxima; then lane cg forms the scale and reciprocal of
+        // row cg & 3 only, and a quad broadcast hands row i's pair to every
+        // lane: one pair of IEEE divisions per lane instead of four.
+        float rm[kTRows];
 #pragma unroll
         for (int i = 0; i < kTRows; ++i) {
             float m = 0.f;
@@ -374,9 +400,15 @@ void swiglu_quant_t_kernel(SwigluArgs a, int64_t tiles, uint8_t* __restrict__ ou
             m = fmaxf(m, tk::dpp_f32<tk::kQuadXor1>(m));
             m = fmaxf(m, tk::dpp_f32<tk::kQuadXor2>(m));
             m = fmaxf(m, tk::dpp_f32<tk::kHalfMirror>(m));
-            m = fmaxf(m, tk::dpp_f32<tk::kMirror>(m));      // the 16 lanes of this row group
-            const float scale = fmaxf(m, 1e-4f) / 448.0f;
-            const float inv = 1.0f / scale;
+            rm[i] = fmaxf(m, tk::dpp_f32<tk::kMirror>(m));   // the 16 lanes of this row group
+        }
+        const int mine = cg & 3;
+        const float m_mine = mine == 0 ? rm[0] : (mine == 1 ? rm[1] : (mine == 2 ? rm[2] : rm[3]));
+        const float s_mine = fmaxf(m_mine, 1e-4f) / 448.0f;
+        const float inv_mine = 1.0f / s_mine;
+#pragma unroll
+        for (int i = 0; i < kTRows; ++i) {
+            const float scale = quad_lane(s_mine, i), inv = quad_lane(inv_mine, i);
             uint2 o;
             o.x = tk::pack_fp8x4(tk::fp8_quotient(v[i][0], scale, inv), tk::fp8_quotient(v[i][1], scale, inv),
                                  tk::fp8_quotient(v[i][2], scale, inv), tk::fp8_quotient(v[i][3], scale, inv));
@@ -386,7 +418,6 @@ void swiglu_quant_t_kernel(SwigluArgs a, int64_t tiles, uint8_t* __restrict__ ou
             *reinterpret_cast<uint2*>(a.out + static_cast<size_t>(r) * a.I + c0 + cg * 8) = o;
             if (cg == 0) a.scales[static_cast<size_t>(r) * (a.I / 128) + tc] = scale;
         }
-        if constexpr (WEIGHTED) load_slots(tok_next);   // the next tile's slots
 
         // transposed codes: one 1x128 block per tile column
         __syncthreads();   // col_part complete; w_row read out
@@ -396,19 +427,20 @@ void swiglu_quant_t_kernel(SwigluArgs a, int64_t tiles, uint8_t* __restrict__ ou
             for (int g = 1; g < kTGroups; ++g) m = fmaxf(m, col_part[g][threadIdx.x]);
             const float scale = fmaxf(m, 1e-4f) / 448.0f;
             col_scale[threadIdx.x] = scale;
+            col_inv[threadIdx.x] = 1.0f / scale;
             scales_t[static_cast<size_t>(c0 + threadIdx.x) * (R / kTile) + tr] = scale;
         }
         __syncthreads();   // col_scale ready, col_part consumed: stage now holds codes
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const float scale = col_scale[cg * 8 + j];
-            const float inv = 1.0f / scale;
+            const float scale = col_scale[cg * 8 + j], inv = col_inv[cg * 8 + j];
             const uint32_t q = tk::pack_fp8x4(tk::fp8_quotient(v[0][j], scale, inv),
                                               tk::fp8_quotient(v[1][j], scale, inv),
                                               tk::fp8_quotient(v[2][j], scale, inv),
                                               tk::fp8_quotient(v[3][j], scale, inv));
             *reinterpret_cast<uint32_t*>(stage + (cg * 8 + j) * kTPitch + rg * kTRows) = q;
         }
+        if constexpr (WEIGHTED) load_slots(tok_next);   // the next tile's slots
         __syncthreads();
         // 128 out_t rows of 128 bytes: 8 threads per row, 16 bytes each
         for (int i = threadIdx.x; i < kTile * 8; i += kTThreads) {

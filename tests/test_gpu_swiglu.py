@@ -208,3 +208,31 @@ def test_silu_bf16_every_value():
     got2 = to_host(tk.tk_silu_bf16(to_dev(many, bf16=True)))
     assert np.array_equal(got2.view(np.uint32)[~np.isnan(got2)],
                           np.resize(got, many.size).view(np.uint32)[~np.isnan(got2)])
+
+
+def test_swiglu_quant_t_v3_expert_shape_column_blocks():
+    """The transposing form at the DeepSeek-V3 expert shape (65536 rows of the
+    step's routing, I = 2048, weighted through the map), as launched by the
+    bench.  Both layouts of a 128-column block depend only on that block's
+    gate and up columns, so the oracle runs on two whole blocks over all rows
+    and is compared bit for bit with those parts of the outputs."""
+    cfg = synth.v3_gate(0)
+    idx, w = oracle.route(cfg["logits"], cfg["bias"], cfg["k"], **cfg["route"])
+    w = w.astype(np.float32)
+    _, offsets, pos, row_src = oracle.map_routes(idx, 256)
+    R, I = int(offsets[-1]), 2048
+    assert R == 65536
+    h = synth.normal_bf16(np.random.default_rng(86), (R, 2 * I))
+    out, sc, out_t, sc_t = tk.tk_swiglu_quant_t(to_dev(h, bf16=True), to_dev(row_src), to_dev(pos),
+                                               to_dev(w))
+    torch.cuda.synchronize()
+    rw = oracle.row_weights(pos, w, R)
+    for c0 in (0, 1920):
+        sub = np.concatenate([h[:, c0:c0 + 128], h[:, I + c0:I + c0 + 128]], axis=1)
+        q_ref, s_ref = oracle.swiglu_quant(sub, 128, rw)
+        qt_ref, st_ref = oracle.swiglu_quant_t(sub, 128, rw)
+        assert np.array_equal(to_host(out[:, c0:c0 + 128].contiguous()), q_ref), c0
+        assert np.array_equal(to_host(sc[:, c0 // 128].contiguous()), s_ref[:, 0]), c0
+        assert np.array_equal(to_host(sc_t[c0:c0 + 128]), st_ref), c0
+        bad = np.argwhere(to_host(out_t[c0:c0 + 128]) != qt_ref)
+        assert bad.size == 0, f"block {c0}: {len(bad)} transposed codes differ, first {bad[:4]}"
