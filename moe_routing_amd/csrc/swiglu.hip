@@ -249,6 +249,11 @@ constexpr int kTRows = 4;                         // rows per thread
 constexpr int kTGroups = kTile / kTRows;          // 32 row groups
 constexpr int kTPitch = kTile + 16;               // bytes per staged out_t row (padded)
 static_assert(kTRows == 4, "a row group's rows are handed out by quad broadcasts");
+// Tile t -> (row tile, column tile): the column tiles of one row tile are
+// consecutive, so workgroups running side by side read whole rows of h.
+__device__ __forceinline__ int64_t tile_row(int64_t t, int tiles_c) { return t / tiles_c; }
+__device__ __forceinline__ int tile_col(int64_t t, int tiles_c) { return static_cast<int>(t % tiles_c); }
+
 // lane i of each lane quad, to all four lanes (DPP quad_perm [i,i,i,i]); i is
 // a compile-time constant after unrolling
 __device__ __forceinline__ float quad_lane(float x, int i)
@@ -324,7 +329,7 @@ void swiglu_quant_t_kernel(SwigluArgs a, int64_t tiles, uint8_t* __restrict__ ou
     };
     if constexpr (WEIGHTED) {
         if (blockIdx.x < tiles) {
-            const int64_t row = blockIdx.x / tiles_c * kTile + wrow;
+            const int64_t row = tile_row(blockIdx.x, tiles_c) * kTile + wrow;
             const int t = a.row_src[row];
             load_slots(t);
             pick_weight(t, row);
@@ -333,12 +338,12 @@ void swiglu_quant_t_kernel(SwigluArgs a, int64_t tiles, uint8_t* __restrict__ ou
     __syncthreads();   // the table and the first tile's weights
 
     for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
-        const int64_t tr = tile / tiles_c;
-        const int tc = static_cast<int>(tile - tr * tiles_c);
+        const int64_t tr = tile_row(tile, tiles_c);
+        const int tc = tile_col(tile, tiles_c);
         const int64_t r0 = tr * kTile;
         const int c0 = tc * kTile;
         const int64_t next = tile + gridDim.x;
-        const int64_t next_row = next / tiles_c * kTile + wrow;
+        const int64_t next_row = tile_row(next, tiles_c) * kTile + wrow;
 
         tk::u32x4 gw[kTRows], uw[kTRows];
 #pragma unroll
