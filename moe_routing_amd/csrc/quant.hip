@@ -29,10 +29,11 @@
 //  - FP4: the matrix as one flat run of values (no block straddles a row);
 //    one wave per 2048 values, one 32-value block per lane quad (16-byte
 //    loads, the wave reading 1 KB contiguous per instruction; one 32-bit
-//    word of codes per lane); E2M1 encoding by integer rounding of the fp32
-//    bits to one mantissa bit (ties to even).
+//    word of codes per lane); E2M1 codes from a compile-time table in LDS
+//    indexed by the quotient's clamped bf16 magnitude.
 // Codes are written with streaming stores; the E4M3 quotient is the shared
 // Markstein-corrected one, exact for power-of-two scales.
+#include "e2m1_table.h"
 #include "tk_internal.h"
 
 namespace {
@@ -263,22 +264,13 @@ __global__ __launch_bounds__(tk::kBlock) void quant_pc_apply_kernel(
 }
 
 // ------------------------------------------------------------------- FP4
-// E2M1 code of v (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), nearest with ties to
-// the even code, saturating at 6, sign kept.  |v| is clamped to 6 and rounded
-// to one mantissa bit in fp32 by integer arithmetic (add 2^21 - 1 plus the
-// kept bit, drop 22 bits: round half to even); the code is then read off the
-// exponent and the kept bit.  Below 1 (the format's subnormal 0.5 step) the
-// value is first shifted by +1.0, which is exact here because the inputs carry
-// at most 8 significant bits, so [0, 1) rounds on the same half-unit grid.
-__device__ __forceinline__ uint32_t e2m1_code(float v)
-{
-    const float a = fminf(fabsf(v), 6.0f);
-    const bool sub = a < 1.0f;
-    uint32_t b = __float_as_uint(sub ? a + 1.0f : a);
-    b += 0x1FFFFFu + ((b >> 22) & 1u);
-    const uint32_t c = (b >> 22) - (sub ? 254u : 252u);
-    return c | ((__float_as_uint(v) >> 28) & 8u);
-}
+// E2M1 codes by table (e2m1_table.h): a quotient x * 2^j of a bf16 input by
+// the block's exact power-of-two reciprocal keeps at most 8 significant bits,
+// so its code is a 640-entry byte table indexed by its clamped bf16 magnitude
+// -- four instructions and one LDS byte read where rounding by arithmetic took
+// about a dozen.  The table is built at compile time.
+__device__ const tk::E2m1Table kE2m1Dev = tk::make_e2m1_table();
+static_assert(tk::kE2m1N % 4 == 0, "the table is copied in 4-byte words");
 
 // The matrix is taken as one flat run of rows * cols values: cols % 32 == 0,
 // so no block straddles a row, and a block's codes and scale sit at flat / 2
@@ -292,16 +284,20 @@ constexpr int kFp4PerWave = 2048;
 __global__ __launch_bounds__(tk::kBlock) void quant_fp4_kernel(
     const uint16_t* __restrict__ x, int64_t n, uint8_t* __restrict__ q, float* __restrict__ scales)
 {
+    __shared__ __align__(4) uint8_t table[tk::kE2m1N];
     const int lane = threadIdx.x & (tk::kWave - 1);
     const int64_t base = (static_cast<int64_t>(blockIdx.x) * tk::kWavesPerBlock +
                           tk::uniform(threadIdx.x / tk::kWave)) * kFp4PerWave;
-    if (base >= n) return;
     tk::u32x4 w[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int64_t f = base + j * 512 + lane * 8;
         w[j] = f < n ? tk::load_stream(x + f) : tk::u32x4{0u, 0u, 0u, 0u};
     }
+    for (int i = threadIdx.x; i < static_cast<int>(tk::kE2m1N / 4); i += tk::kBlock)
+        reinterpret_cast<uint32_t*>(table)[i] = reinterpret_cast<const uint32_t*>(kE2m1Dev.code)[i];
+    __syncthreads();
+    if (base >= n) return;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int64_t f = base + j * 512 + lane * 8;   // n % 32 == 0: quads are wholly in or out
@@ -319,7 +315,7 @@ __global__ __launch_bounds__(tk::kBlock) void quant_fp4_kernel(
         const float inv = __builtin_ldexpf(1.0f, 3 - e);       // exact
         uint32_t p = 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) p |= e2m1_code(v[i] * inv) << (4 * i);
+        for (int i = 0; i < 8; ++i) p |= tk::e2m1_lookup(__float_as_uint(v[i] * inv), table) << (4 * i);
         if (f < n) {
             __builtin_nontemporal_store(p, reinterpret_cast<uint32_t*>(q + f / 2));
             if ((lane & 3) == 0) scales[f / 32] = scale;
