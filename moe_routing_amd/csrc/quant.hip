@@ -22,10 +22,11 @@
 //    patch (eight 16-byte row loads), the tile amax is a DPP wave max then an
 //    LDS step over the four waves.
 //  - per-channel: workgroups of 256 columns x 8 row groups.  Pass 1 takes
-//    column maxima over chunks of 128 rows (16 rows per thread, 8 loads in
-//    flight, row groups combined in LDS) into the workspace; pass 2 takes
-//    the maximum over the chunks (exact in any order), forms the scales and
-//    quantises 64 rows per workgroup.
+//    column maxima over chunks of 128 rows (16 rows per thread, 8 streaming
+//    loads in flight, row groups combined in LDS) into the workspace; a small
+//    pass takes the maximum over the chunks (exact in any order) per column
+//    and forms the scale and its reciprocal; the last pass quantises 64 rows
+//    per workgroup with them.
 //  - FP4: the matrix as one flat run of values (no block straddles a row);
 //    one wave per 2048 values, one 32-value block per lane quad (16-byte
 //    loads, the wave reading 1 KB contiguous per instruction; one 32-bit
@@ -178,7 +179,7 @@ __global__ __launch_bounds__(tk::kBlock) void quant_pc_partial_kernel(
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             w[i] = tk::u32x4{0u, 0u, 0u, 0u};
-            if (active && r0 + i0 + i < rows) w[i] = tk::load16(x + static_cast<size_t>(r0 + i0 + i) * cols + col);
+            if (active && r0 + i0 + i < rows) w[i] = tk::load_stream(x + static_cast<size_t>(r0 + i0 + i) * cols + col);
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -203,44 +204,52 @@ __global__ __launch_bounds__(tk::kBlock) void quant_pc_partial_kernel(
     }
 }
 
-// scales from the maxima over all chunks, then the codes of kPcRowsPerBlock rows
-__global__ __launch_bounds__(tk::kBlock) void quant_pc_apply_kernel(
-    const uint16_t* __restrict__ x, int64_t rows, int cols, int n_chunks,
-    const float* __restrict__ partial, uint8_t* __restrict__ q, float* __restrict__ scales)
+// Per column: the maximum over all chunks, the scale (written to scales) and
+// its reciprocal (workspace, after the chunk maxima).  A workgroup takes 32
+// columns; its 8 thread groups split the chunks (group g: chunks g, g+8, ...,
+// eight loads in flight per batch, each a coalesced 128-byte row piece) and
+// combine in LDS.
+constexpr int kPsCols = 32;
+constexpr int kPsGroups = tk::kBlock / kPsCols;   // 8
+
+__global__ __launch_bounds__(tk::kBlock) void quant_pc_scale_kernel(
+    const float* __restrict__ partial, int cols, int n_chunks, float* __restrict__ scales,
+    float* __restrict__ inv_out)
 {
-    __shared__ float red[kPcRowGroups][kPcCols];
-    const int cgi = threadIdx.x & 31, rg = threadIdx.x >> 5;
-    const int col = blockIdx.x * kPcCols + cgi * 8;
-    const bool active = col < cols;
-    float s[8];
+    __shared__ float red[kPsGroups][kPsCols];
+    const int cl = threadIdx.x % kPsCols, g = threadIdx.x / kPsCols;
+    const int c = blockIdx.x * kPsCols + cl;
+    float m = 0.f;
+    if (c < cols) {
+        for (int b = g; b < n_chunks; b += kPsGroups * 8) {
+            float t[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) s[j] = 0.f;
-    if (active) {
-        for (int ch = rg; ch < n_chunks; ch += kPcRowGroups) {   // row group g takes chunks g, g+8, ...
-            const float* p = partial + static_cast<size_t>(ch) * cols + col;
-            const float4 a = *reinterpret_cast<const float4*>(p);
-            const float4 b = *reinterpret_cast<const float4*>(p + 4);
-            s[0] = fmaxf(s[0], a.x); s[1] = fmaxf(s[1], a.y); s[2] = fmaxf(s[2], a.z); s[3] = fmaxf(s[3], a.w);
-            s[4] = fmaxf(s[4], b.x); s[5] = fmaxf(s[5], b.y); s[6] = fmaxf(s[6], b.z); s[7] = fmaxf(s[7], b.w);
+            for (int u = 0; u < 8; ++u) {
+                const int ch = b + u * kPsGroups;
+                t[u] = ch < n_chunks ? partial[static_cast<size_t>(ch) * cols + c] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) m = fmaxf(m, t[u]);
         }
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) red[rg][cgi * 8 + j] = s[j];
+    red[g][cl] = m;
     __syncthreads();
-    float inv[8];
+    if (g != 0 || c >= cols) return;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        float m = red[0][cgi * 8 + j];
-#pragma unroll
-        for (int g = 1; g < kPcRowGroups; ++g) m = fmaxf(m, red[g][cgi * 8 + j]);
-        s[j] = fmaxf(m, 1e-4f) / 448.0f;
-        inv[j] = 1.0f / s[j];
-    }
-    if (!active) return;
-    if (blockIdx.y == 0 && rg == 0) {
-        *reinterpret_cast<float4*>(scales + col) = make_float4(s[0], s[1], s[2], s[3]);
-        *reinterpret_cast<float4*>(scales + col + 4) = make_float4(s[4], s[5], s[6], s[7]);
-    }
+    for (int k = 1; k < kPsGroups; ++k) m = fmaxf(m, red[k][cl]);
+    const float s = fmaxf(m, 1e-4f) / 448.0f;
+    scales[c] = s;
+    inv_out[c] = 1.0f / s;
+}
+
+// the codes of kPcRowsPerBlock rows from the per-column scales and reciprocals
+__global__ __launch_bounds__(tk::kBlock) void quant_pc_apply_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int cols, const float* __restrict__ scales,
+    const float* __restrict__ inv_in, uint8_t* __restrict__ q)
+{
+    const int cgi = threadIdx.x & 31, rg = threadIdx.x >> 5;
+    const int col = blockIdx.x * kPcCols + cgi * 8;
+    if (col >= cols) return;
     const int rows_per_group = kPcRowsPerBlock / kPcRowGroups;   // 8
     const int64_t r0 = static_cast<int64_t>(blockIdx.y) * kPcRowsPerBlock + rg * rows_per_group;
     tk::u32x4 w[8];
@@ -249,6 +258,12 @@ __global__ __launch_bounds__(tk::kBlock) void quant_pc_apply_kernel(
         w[i] = tk::u32x4{0u, 0u, 0u, 0u};
         if (i < rows_per_group && r0 + i < rows) w[i] = tk::load_stream(x + static_cast<size_t>(r0 + i) * cols + col);
     }
+    const float4 sa = *reinterpret_cast<const float4*>(scales + col);
+    const float4 sb = *reinterpret_cast<const float4*>(scales + col + 4);
+    const float4 ia = *reinterpret_cast<const float4*>(inv_in + col);
+    const float4 ib = *reinterpret_cast<const float4*>(inv_in + col + 4);
+    const float s[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+    const float inv[8] = {ia.x, ia.y, ia.z, ia.w, ib.x, ib.y, ib.z, ib.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         if (i >= rows_per_group || r0 + i >= rows) break;
@@ -331,7 +346,8 @@ TK_EXPORT size_t tk_quant_workspace_bytes(int64_t rows, int32_t cols, int32_t mo
 {
     if (mode != TK_QUANT_FP8_PER_CHANNEL || rows <= 0 || cols <= 0) return 0;
     const int64_t n_chunks = (rows + kPcRowsPerChunk - 1) / kPcRowsPerChunk;
-    return static_cast<size_t>(n_chunks) * static_cast<size_t>(cols) * sizeof(float);
+    // the chunk maxima, then one row of reciprocal scales
+    return static_cast<size_t>(n_chunks + 1) * static_cast<size_t>(cols) * sizeof(float);
 }
 
 TK_EXPORT tk_status tk_quant(const void* x_bf16, int64_t rows, int32_t cols, int32_t mode,
@@ -384,11 +400,15 @@ TK_EXPORT tk_status tk_quant(const void* x_bf16, int64_t rows, int32_t cols, int
             return fail(TK_ERR_UNSUPPORTED, "tk_quant: too many rows for per-channel");
         const unsigned gx = static_cast<unsigned>((cols + kPcCols - 1) / kPcCols);
         auto* partial = static_cast<float*>(workspace);
+        float* inv = partial + static_cast<size_t>(n_chunks) * cols;
         e = tk::launch(quant_pc_partial_kernel, dim3(gx, static_cast<unsigned>(n_chunks)), block, 0,
                        stream, x, rows, cols, partial);
         if (e != hipSuccess) return tk::launched(e, "tk_quant (per-channel maxima)");
+        e = tk::launch(quant_pc_scale_kernel, dim3(static_cast<unsigned>((cols + kPsCols - 1) / kPsCols)),
+                       block, 0, stream, partial, cols, static_cast<int>(n_chunks), scales, inv);
+        if (e != hipSuccess) return tk::launched(e, "tk_quant (per-channel scales)");
         e = tk::launch(quant_pc_apply_kernel, dim3(gx, static_cast<unsigned>(n_blocks)), block, 0,
-                       stream, x, rows, cols, static_cast<int>(n_chunks), partial, q, scales);
+                       stream, x, rows, cols, scales, inv, q);
     } else {
         const int64_t n = rows * cols;
         const int64_t waves = (n + kFp4PerWave - 1) / kFp4PerWave;

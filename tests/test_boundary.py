@@ -257,7 +257,7 @@ def test_quant_rejects_bad_arguments(lib):
     assert b"workspace" in lib.tk_last_error()
     assert call(0, 256, 0, x=None, out=None, sc=None) == 0
     f = lib.tk_quant_workspace_bytes
-    assert f(I64(1000), I(256), I(3)) == 8 * 256 * 4      # 8 chunks of 128 rows
+    assert f(I64(1000), I(256), I(3)) == 9 * 256 * 4      # 8 chunks of 128 rows + reciprocals
     assert f(I64(1000), I(256), I(0)) == 0
 
 
