@@ -155,6 +155,40 @@ def bench_swiglu(tk, torch, y, n_rows, row_src, pos, w, steps):
             "transposed": transposed}
 
 
+def stream_copy_gbps(torch, dev, reps: int = 10):
+    """Bandwidth of the repository's streaming copy kernel over 1 GiB: read +
+    written bytes per second (the reference for what a plain copy reaches)."""
+    import ctypes
+    from moe_routing_amd import _build
+    if not os.path.exists(_build.CALIB_LIB):
+        return None
+    lib = ctypes.CDLL(_build.CALIB_LIB)
+    lib.tk_calib_stream_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                         ctypes.c_void_p]
+    lib.tk_calib_stream_copy.restype = ctypes.c_int
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def copy():
+        if lib.tk_calib_stream_copy(src.data_ptr(), dst.data_ptr(), n, stream) != 0:
+            raise RuntimeError("stream copy failed")
+
+    copy()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        copy()
+    b.record()
+    torch.cuda.synchronize()
+    if not torch.equal(src[:4096], dst[:4096]) or not torch.equal(src[-4096:], dst[-4096:]):
+        raise RuntimeError("stream copy wrote wrong bytes")
+    return 2.0 * n * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+
+
 def _time_calls(torch, call, steps, outputs):
     """GPU time per call of a short, launch-bound call: `steps` calls are
     captured in one HIP graph and the graph is replayed, so the host-side cost
@@ -342,6 +376,28 @@ def main() -> int:
             per[s].append(e[j].elapsed_time(e[j + 1]))
     kern_us = {s: 1e3 * float(np.mean(v)) for s, v in per.items()}
     kern_med_us = {s: 1e3 * float(np.median(v)) for s, v in per.items()}
+    kern_p10_us = {s: 1e3 * float(np.percentile(v, 10)) for s, v in per.items()}
+    kern_p90_us = {s: 1e3 * float(np.percentile(v, 90)) for s, v in per.items()}
+
+    # Cold caches: before each of these passes a 1 GiB read evicts the MALL
+    # (256 MB) and the L2s, so no input of the step is cached when it starts.
+    # A read, not a write: a write would leave up to 256 MB of dirty lines
+    # whose write-back the timed step would pay for; the read also drains the
+    # previous pass's own dirty lines before the timer starts.
+    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    cold, cold_per = [], {s: [] for s in steps}
+    for _ in range(min(args.steps, 10)):
+        flush.sum()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        step(ev)
+        torch.cuda.synchronize()
+        cold.append(ev[0].elapsed_time(ev[4]))
+        for j, s in enumerate(steps):
+            cold_per[s].append(ev[j].elapsed_time(ev[j + 1]))
+    cold_ms = float(np.median(cold))
+    cold_kern_us = {s: 1e3 * float(np.median(v)) for s, v in cold_per.items()}
+    del flush
+    copy_gbps = stream_copy_gbps(torch, dev)
 
     if args.calib_copy:
         # a plain device copy of known size, for scaling the HBM byte counters
@@ -384,6 +440,18 @@ def main() -> int:
         "algorithmic_bytes_per_step": BYTES["total"],
         "kernel_us_mean": {s: round(v, 2) for s, v in kern_us.items()},
         "kernel_us_median": {s: round(v, 2) for s, v in kern_med_us.items()},
+        "kernel_us_p10": {s: round(v, 2) for s, v in kern_p10_us.items()},
+        "kernel_us_p90": {s: round(v, 2) for s, v in kern_p90_us.items()},
+        "cold_cache": {"ms_per_step_median": round(cold_ms, 5), "steps": len(cold),
+                       "kernel_us_median": {s: round(v, 2) for s, v in cold_kern_us.items()},
+                       "hbm_frac": round(BYTES["total"] / (cold_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                       "flush": "1 GiB device read before each step; events between the calls "
+                                "as in the breakdown pass"},
+        "stream_copy": None if copy_gbps is None else {
+            "gbps": round(copy_gbps, 1),
+            "what": "in-repository streaming copy kernel (libtk_calib.so), 1 GiB, read + written "
+                    "bytes over time",
+            "pipeline_frac_of_copy": round(gbps / copy_gbps, 4)},
         "kernel_gbps": {s: round(BYTES[s] / (kern_us[s] * 1e-6) / 1e9, 1) for s in steps},
         "wall_s_timed": round(wall, 4),
         "kernel_breakdown": "second pass of the same steps with an event between calls",

@@ -3,7 +3,9 @@
 First a host-only generator (sigmoid_table_gen.hip) is compiled and run: it
 writes _build/sigmoid_table.inc, the pinned sigmoid at every bf16 value of
 its band, which swiglu.hip includes.  Then each .hip source is compiled to an
-object under _build/ in parallel and linked into moe_routing_amd/libtk.so.
+object under _build/ in parallel and linked into moe_routing_amd/libtk.so;
+calib.hip (a streaming copy bench.py measures for reference) becomes
+moe_routing_amd/libtk_calib.so.
 Always recompiles (a build check must compile); callers that only need the
 library load it when it exists.
 """
@@ -19,6 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtk.so")
+CALIB_LIB = os.path.join(PKG, "libtk_calib.so")   # bench.py's stream-copy reference
 SOURCES = ["api.hip", "route.hip", "map.hip", "expand.hip", "reduce.hip", "swiglu.hip", "balance.hip", "quant.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -69,8 +72,15 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    obj = _compile("calib.hip")
+    tmp = CALIB_LIB + ".tmp"
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", obj, "-o", tmp],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed (calib):\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, CALIB_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CALIB_LIB}")
     return LIB
 
 

@@ -286,3 +286,21 @@ def test_silu_rejects_bad_arguments(lib):
     assert f(FAKE, I64(4), MIS1, None) == ARG         # out not 4-byte aligned
     assert f(MIS1, I64(4), FAKE, None) == ARG         # g not 2-byte aligned
     assert f(None, I64(0), None, None) == 0
+
+
+def test_calibration_library_exports_only_the_stream_copy():
+    """bench.py's reference copy lives in its own library, outside the routing ABI."""
+    import subprocess
+    from moe_routing_amd import _build
+    if not os.path.exists(_build.CALIB_LIB):
+        pytest.skip("library not built")
+    out = subprocess.run(["nm", "-D", "--defined-only", _build.CALIB_LIB], capture_output=True,
+                         text=True).stdout
+    assert {l.split()[-1] for l in out.splitlines() if " T " in l} == {"tk_calib_stream_copy"}
+    lib = ctypes.CDLL(_build.CALIB_LIB)
+    f = lib.tk_calib_stream_copy
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    assert f(None, None, 0, None) == 0                       # nothing to copy
+    assert f(FAKE, FAKE, 24, None) == -1                     # not a multiple of 16
+    assert f(MIS, FAKE, 32, None) == -1                      # misaligned source
+    assert f(None, FAKE, 32, None) == -1
