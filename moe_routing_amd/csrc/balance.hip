@@ -15,9 +15,14 @@
 //               each wave accumulates p over its tokens in token order, the
 //               workgroup adds its waves in wave order -> part_p[tile][e];
 //               LDS integer histogram of the tile's routes -> part_c[tile][e]
-//   2. final    one workgroup: per expert, the tiles in order (four threads
-//               per expert over quarters of the tiles, added in quarter
-//               order), then f, P, and the loss accumulated in fp64.
+//   2. final    a workgroup per 32 experts: eight thread groups per expert
+//               take the tiles g, g+8, ... in order and are added in group
+//               order, giving f and P; the last workgroup to finish (a
+//               counter in the workspace, zeroed by the partial pass) then
+//               sums f*P over all experts in fp64, in expert order.  The
+//               last one reads every other workgroup's f and P after their
+//               release fences, so the loss does not depend on which
+//               workgroup it is.
 #include "tk_internal.h"
 
 namespace {
@@ -25,15 +30,17 @@ namespace {
 constexpr int kTileTokens = 32;      // tokens per partial workgroup (4 per wave)
 constexpr int kPartialWaves = 8;
 constexpr int kPartialThreads = kPartialWaves * 64;
-constexpr int kFinalThreads = 1024;
-constexpr int kParts = 4;            // threads per expert in the final pass
+constexpr int kFinalThreads = 256;
+constexpr int kFinalExperts = 32;                          // experts per final workgroup
+constexpr int kFinalGroups = kFinalThreads / kFinalExperts;  // 8 tile groups
 
 template <int EPL, bool SIGMOID>
 __global__ __launch_bounds__(kPartialThreads) void balance_partial_kernel(
     const float* __restrict__ logits, const int32_t* __restrict__ idx, int T, int E, int k,
-    float* __restrict__ part_p, int32_t* __restrict__ part_c)
+    float* __restrict__ part_p, int32_t* __restrict__ part_c, uint32_t* __restrict__ done)
 {
     __shared__ float wave_acc[kPartialWaves][tk::kWave * EPL];
+    if (blockIdx.x == 0 && threadIdx.x == 0) *done = 0u;   // the final pass counts on it
     extern __shared__ int32_t hist[];
     const int lane = threadIdx.x & (tk::kWave - 1);
     const int wave = tk::uniform(threadIdx.x / tk::kWave);
@@ -94,53 +101,61 @@ __global__ __launch_bounds__(kPartialThreads) void balance_partial_kernel(
 
 __global__ __launch_bounds__(kFinalThreads) void balance_final_kernel(
     const float* __restrict__ part_p, const int32_t* __restrict__ part_c, int n_tiles, int T,
-    int E, int k, float* __restrict__ f, float* __restrict__ P, float* __restrict__ loss)
+    int E, int k, float* __restrict__ f, float* __restrict__ P, float* __restrict__ loss,
+    uint32_t* __restrict__ done)
 {
-    __shared__ float sp[kParts][TK_MAX_EXPERTS / kParts * kParts];
-    __shared__ int32_t sc[kParts][TK_MAX_EXPERTS / kParts * kParts];
+    __shared__ float sp[kFinalGroups][kFinalExperts];
+    __shared__ int32_t sc[kFinalGroups][kFinalExperts];
     __shared__ double red[kFinalThreads];
-    // thread (part, e) sums tiles [part*n/4, (part+1)*n/4) of expert e, in order
-    const int per = (n_tiles + kParts - 1) / kParts;
-    for (int i = threadIdx.x; i < kParts * E; i += kFinalThreads) {
-        const int part = i / E, e = i - part * E;
-        float v = 0.f;
-        int32_t c = 0;
-        const int a = part * per, b = min(n_tiles, a + per);
-        for (int t0 = a; t0 < b; t0 += 8) {   // eight tiles' loads in flight, summed in order
+    __shared__ bool last;
+    const int cl = threadIdx.x % kFinalExperts, g = threadIdx.x / kFinalExperts;
+    const int e = blockIdx.x * kFinalExperts + cl;
+    float v = 0.f;
+    int32_t c = 0;
+    if (e < E) {
+        for (int t0 = g; t0 < n_tiles; t0 += kFinalGroups * 8) {   // eight tiles' loads in flight
             float pv[8];
             int32_t cv[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const bool in = t0 + i < b;
-                pv[i] = in ? part_p[static_cast<size_t>(t0 + i) * E + e] : 0.f;
-                cv[i] = in ? part_c[static_cast<size_t>(t0 + i) * E + e] : 0;
+                const int t = t0 + i * kFinalGroups;
+                pv[i] = t < n_tiles ? part_p[static_cast<size_t>(t) * E + e] : 0.f;
+                cv[i] = t < n_tiles ? part_c[static_cast<size_t>(t) * E + e] : 0;
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                if (t0 + i < b) {
+                if (t0 + i * kFinalGroups < n_tiles) {
                     v += pv[i];
                     c += cv[i];
                 }
             }
         }
-        sp[part][e] = v;
-        sc[part][e] = c;
     }
+    sp[g][cl] = v;
+    sc[g][cl] = c;
     __syncthreads();
     const double scale = static_cast<double>(E) / (static_cast<double>(k) * static_cast<double>(T));
-    double my = 0.0;
-    for (int e = threadIdx.x; e < E; e += kFinalThreads) {
-        float v = sp[0][e];
-        int64_t c = sc[0][e];
+    if (g == 0 && e < E) {
+        int64_t cnt = c;
 #pragma unroll
-        for (int part = 1; part < kParts; ++part) {
-            v += sp[part][e];
-            c += sc[part][e];
+        for (int h = 1; h < kFinalGroups; ++h) {
+            v += sp[h][cl];
+            cnt += sc[h][cl];
         }
-        const float pe = v / static_cast<float>(T);
-        const float fe = static_cast<float>(scale * static_cast<double>(c));
-        P[e] = pe;
-        f[e] = fe;
+        P[e] = v / static_cast<float>(T);
+        f[e] = static_cast<float>(scale * static_cast<double>(cnt));
+    }
+    // the last workgroup to get here forms the loss from every workgroup's f and P
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) last = atomicAdd(done, 1u) == gridDim.x - 1;
+    __syncthreads();
+    if (!last) return;
+    __threadfence();
+    double my = 0.0;
+    for (int i = threadIdx.x; i < E; i += kFinalThreads) {
+        const float fe = __hip_atomic_load(f + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float pe = __hip_atomic_load(P + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         my += static_cast<double>(fe) * static_cast<double>(pe);
     }
     red[threadIdx.x] = my;
@@ -165,7 +180,8 @@ TK_EXPORT size_t tk_balance_workspace_bytes(int32_t T, int32_t E)
 {
     if (T <= 0 || E <= 0) return 0;
     const size_t n_tiles = (static_cast<size_t>(T) + kTileTokens - 1) / kTileTokens;
-    return n_tiles * static_cast<size_t>(E) * (sizeof(float) + sizeof(int32_t));
+    // per-tile partial sums and counts, then the final pass's counter
+    return n_tiles * static_cast<size_t>(E) * (sizeof(float) + sizeof(int32_t)) + 16;
 }
 
 TK_EXPORT tk_status tk_balance_loss(const float* logits, const int32_t* topk_idx, int32_t T,
@@ -193,15 +209,16 @@ TK_EXPORT tk_status tk_balance_loss(const float* logits, const int32_t* topk_idx
     const int n_tiles = (T + kTileTokens - 1) / kTileTokens;
     float* part_p = static_cast<float*>(workspace);
     int32_t* part_c = reinterpret_cast<int32_t*>(part_p + static_cast<size_t>(n_tiles) * E);
+    auto* done = reinterpret_cast<uint32_t*>(part_c + static_cast<size_t>(n_tiles) * E);
     const dim3 grid(n_tiles), block(kPartialThreads);
     const size_t lds = static_cast<size_t>(E) * sizeof(int32_t);
     const bool sig = score == TK_SCORE_SIGMOID;
     hipError_t e;
 #define TK_BALANCE(EPL_)                                                                           \
     e = sig ? tk::launch(balance_partial_kernel<EPL_, true>, grid, block, lds, stream, logits,     \
-                         topk_idx, T, E, k, part_p, part_c)                                        \
+                         topk_idx, T, E, k, part_p, part_c, done)                                  \
             : tk::launch(balance_partial_kernel<EPL_, false>, grid, block, lds, stream, logits,    \
-                         topk_idx, T, E, k, part_p, part_c)
+                         topk_idx, T, E, k, part_p, part_c, done)
     switch (experts_per_lane(E)) {
     case 1: TK_BALANCE(1); break;
     case 2: TK_BALANCE(2); break;
@@ -211,7 +228,7 @@ TK_EXPORT tk_status tk_balance_loss(const float* logits, const int32_t* topk_idx
     }
 #undef TK_BALANCE
     if (e != hipSuccess) return tk::launched(e, "tk_balance_loss (partial)");
-    e = tk::launch(balance_final_kernel, dim3(1), dim3(kFinalThreads), 0, stream, part_p, part_c,
-                   n_tiles, T, E, k, f, P, loss);
+    e = tk::launch(balance_final_kernel, dim3((E + kFinalExperts - 1) / kFinalExperts),
+                   dim3(kFinalThreads), 0, stream, part_p, part_c, n_tiles, T, E, k, f, P, loss, done);
     return tk::launched(e, "tk_balance_loss (final)");
 }

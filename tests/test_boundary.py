@@ -236,7 +236,7 @@ def test_balance_rejects_bad_arguments(lib):
     assert call(8192, 256, 8, 1, wsb=ctypes.c_size_t(10)) == ARG
     assert b"workspace" in lib.tk_last_error()
     assert call(16, 256, 8, 1, w=MIS1) == ARG
-    assert lib.tk_balance_workspace_bytes(I(8192), I(256)) == 256 * 256 * 8   # 256 tiles of 32
+    assert lib.tk_balance_workspace_bytes(I(8192), I(256)) == 256 * 256 * 8 + 16   # 256 tiles of 32 + counter
     assert lib.tk_balance_workspace_bytes(I(0), I(256)) == 0
 
 
