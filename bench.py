@@ -15,13 +15,17 @@ hidden states with 1 % outlier rows x50, bf16 N(0,1) expert outputs) and
 resident in HBM before the timed region.  The expert GEMMs are not part of
 the path: the reduce consumes a fixed expert-output tensor.
 
-Prints ONE JSON line: routed tokens/s (value), the pipeline's algorithmic
-HBM GB/s, per-kernel times from HIP events recorded on the launch stream, the
-roofline of the dominant kernel (the reduce) and the CPU oracle's rate.
-Steps beyond the routing path (next_rows) are timed separately on the same
-data and do not enter value: SwiGLU + 1x128 FP8 quantisation of the 65536
-expanded rows at the DeepSeek-V3 expert width I = 2048, weighted by the
-routing weights through the step's map.
+Prints ONE JSON line: routed tokens/s (value, back-to-back steps), the
+pipeline's algorithmic HBM GB/s, per-kernel times from HIP events recorded on
+the launch stream (mean, median, p10, p90), the same step with the MALL and
+L2 evicted before each pass (cold_cache), the rate of the repository's
+streaming copy kernel for reference (stream_copy), the roofline of the
+dominant kernel (the reduce) and the CPU oracle's rate.  Steps beyond the
+routing path (next_rows) are timed separately on the same data and do not
+enter value: SwiGLU + 1x128 FP8 quantisation of the 65536 expanded rows at
+the DeepSeek-V3 expert width I = 2048 (plain and transposing), weighted by the
+routing weights through the step's map; the padded map; the balance loss; and
+the other quantisation granularities of the hidden states.
 """
 from __future__ import annotations
 
