@@ -6,6 +6,8 @@
  *   tk_route         top-k expert gating and scoring        (logits -> idx, w)
  *   tk_map           token-to-expert mapping                (idx -> counts,
  *                                                            offsets, pos)
+ *   tk_map_aligned   the same with every expert segment     (idx -> counts,
+ *                    padded for a grouped GEMM                 offsets, pos)
  *   tk_expand_quant  expand into expert-contiguous rows,    (x -> rows [+ FP8
  *                    optionally fused 1x128 FP8 E4M3 quant    scales])
  *   tk_reduce        weighted combine back to tokens        (rows, w -> out)
@@ -24,6 +26,10 @@
  *
  *   tk_swiglu_quant  SwiGLU + 1x128 FP8 quantisation        (rows -> codes,
  *                    (+ routing weight)                        scales)
+ *   tk_swiglu_quant_t  the same plus the transposed layout  (rows -> codes,
+ *                    (1x128 blocks along tokens)               scales, both
+ *                                                              layouts)
+ *   tk_silu_bf16     the SwiGLU gate factor g * sigmoid(g)  (bf16 -> fp32)
  *
  * plus tk_expert_standin, a dequantise-and-scale harness kernel that stands in
  * for the expert computation in end-to-end tests.
@@ -51,7 +57,8 @@
  *    kernels do not implement) and launches nothing.  A HIP launch error
  *    returns TK_ERR_DEVICE.  tk_last_error() then describes the failure.
  *    The library never aborts or exits.
- *  - T == 0 is a valid no-op for every call.
+ *  - T == 0 (no tokens) is a valid no-op for every call that takes T, except
+ *    tk_balance_loss, whose statistics are not defined without tokens.
  *  - Device data that breaks a call's contract (an expert id out of range, a
  *    row index beyond the capacity) never causes an out-of-bounds access:
  *    the affected route or row is skipped as documented per call.
