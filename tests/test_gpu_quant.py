@@ -84,8 +84,7 @@ def test_fp4_midpoints():
     assert np.all(s == 1.0)
 
 
-@pytest.mark.parametrize("mode", [tk.TK_QUANT_FP8_1X128_POW2, tk.TK_QUANT_FP8_PER_CHANNEL,
-                                  tk.TK_QUANT_FP4_1X32])
+@pytest.mark.parametrize("mode", MODES)
 def test_quant_v3_hidden_full(mode):
     _check(synth.v3_hidden(0), mode)
 
