@@ -24,8 +24,9 @@ dominant kernel (the reduce) and the CPU oracle's rate.  Steps beyond the
 routing path (next_rows) are timed separately on the same data and do not
 enter value: SwiGLU + 1x128 FP8 quantisation of the 65536 expanded rows at
 the DeepSeek-V3 expert width I = 2048 (plain and transposing), weighted by the
-routing weights through the step's map; the padded map; the balance loss; and
-the other quantisation granularities of the hidden states.
+routing weights through the step's map; the padded map; the balance loss;
+the other quantisation granularities of the hidden states; and the expand
+without quantisation (bf16 rows).
 """
 from __future__ import annotations
 
@@ -256,6 +257,21 @@ def bench_map_balance(tk, torch, logits, idx, steps):
                              "bound": "latency (two dependent launches)"}}
 
 
+def bench_expand_bf16(tk, torch, x, pos, steps):
+    """The expand without quantisation (bf16 rows), on the step's routing."""
+    out = torch.empty((R, H), dtype=torch.bfloat16, device=x.device)
+    us = _time_calls(torch, lambda: tk.tk_expand_quant(x, pos, tk.TK_EXPAND_BF16, R, out),
+                     min(steps, 20), (out,))
+    nbytes = T * H * 2 + R * H * 2 + T * K * 4
+    del out
+    return {"expand_bf16": {"workload": f"x bf16 ({T}, {H}) -> {R} bf16 rows, the step's routing",
+                            "us_per_call": round(us, 2), "timing": "HIP graph of the calls",
+                            "roofline": {"bound": "hbm", "achieved": round(nbytes / us / 1e3, 1),
+                                         "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                         "frac": round(nbytes / us / 1e3 / PEAK_HBM_GBPS, 4),
+                                         "algorithmic_bytes": nbytes}}}
+
+
 def bench_quant(tk, torch, x, steps):
     """Each codec granularity on the step's hidden states (8192 x 7168 bf16)."""
     out = {}
@@ -414,7 +430,8 @@ def main() -> int:
     next_rows = {"swiglu_quant_fp8": bench_swiglu(tk, torch, y, offsets[E:], row_src, pos, w,
                                                   args.steps),
                  **bench_map_balance(tk, torch, logits, idx, args.steps),
-                 **bench_quant(tk, torch, x, args.steps)}
+                 **bench_quant(tk, torch, x, args.steps),
+                 **bench_expand_bf16(tk, torch, x, pos, args.steps)}
 
     ms_per_step = total_ms / args.steps
     value = T / (ms_per_step * 1e-3)
