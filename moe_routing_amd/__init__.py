@@ -21,6 +21,7 @@ step of the path runs in the library's HIP kernels; there is no fallback.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from dataclasses import dataclass
 
@@ -121,17 +122,25 @@ def _ptr(t: torch.Tensor | None):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int | None = None):
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int | None = None,
+         numel: int | None = None, device: torch.device | None = None):
+    """Check a tensor handed to the library: a contiguous HIP tensor of `dtype`,
+    with at least `numel` elements (the extent the C call reads or writes; the
+    library cannot see tensor sizes) on `device`."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the other tensors on {device}")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, the call needs {numel}")
     return t
 
 
@@ -143,14 +152,15 @@ def tk_route(logits: torch.Tensor, bias: torch.Tensor | None, k: int, opts: Rout
              topk_idx: torch.Tensor | None = None, topk_w: torch.Tensor | None = None):
     _dev(logits, "logits", torch.float32, 2)
     T, E = logits.shape
+    dev = logits.device
     if bias is not None:
-        _dev(bias, "bias", torch.float32, 1)
+        _dev(bias, "bias", torch.float32, 1, E, dev)
     if topk_idx is None:
-        topk_idx = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     if topk_w is None:
-        topk_w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
-    _dev(topk_idx, "topk_idx", torch.int32)
-    _dev(topk_w, "topk_w", torch.float32)
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _dev(topk_idx, "topk_idx", torch.int32, numel=T * k, device=dev)
+    _dev(topk_w, "topk_w", torch.float32, numel=T * k, device=dev)
     c = opts._c()
     _check("tk_route", library().tk_route(_ptr(logits), _ptr(bias), T, E, k, ctypes.byref(c),
                                           _ptr(topk_idx), _ptr(topk_w), _stream(logits)))
@@ -187,11 +197,13 @@ def tk_map_aligned(topk_idx: torch.Tensor, E: int, local_begin: int = 0,
     need = tk_map_workspace_bytes(T, k, nl) if nl > 0 else 0
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-    for name, t in (("counts", counts), ("offsets", offsets), ("pos", pos)):
-        _dev(t, name, torch.int32)
-    if row_src is not None:
-        _dev(row_src, "row_src", torch.int32)
-    _dev(workspace, "workspace", torch.uint8)
+    for name, t, n in (("counts", counts, max(nl, 0)), ("offsets", offsets, max(nl, 0) + 1),
+                       ("pos", pos, T * k)):
+        _dev(t, name, torch.int32, numel=n, device=dev)
+    if row_src is not None:   # up to T*k rows plus each local segment's padding
+        _dev(row_src, "row_src", torch.int32, numel=T * k + max(nl, 0) * max(align - 1, 0),
+             device=dev)
+    _dev(workspace, "workspace", torch.uint8, device=dev)
     _check("tk_map", library().tk_map_aligned(
         _ptr(topk_idx), T, k, E, local_begin, local_end, align, _ptr(counts), _ptr(offsets),
         _ptr(pos), _ptr(row_src), _ptr(workspace), workspace.numel(), _stream(topk_idx)))
@@ -201,25 +213,23 @@ def tk_map_aligned(topk_idx: torch.Tensor, E: int, local_begin: int = 0,
 def tk_expand_quant(x: torch.Tensor, pos: torch.Tensor, mode: int, rows_capacity: int,
                     out: torch.Tensor | None = None, scales: torch.Tensor | None = None):
     _dev(x, "x", torch.bfloat16, 2)
-    _dev(pos, "pos", torch.int32, 2)
     T, H = x.shape
+    dev = x.device
+    _dev(pos, "pos", torch.int32, 2, device=dev)
     k = pos.shape[1]
     if pos.shape[0] != T:
         raise ValueError("pos must have one row per token")
-    dev = x.device
     if mode == TK_EXPAND_FP8_E4M3_1X128:
         if out is None:
             out = torch.empty((rows_capacity, H), dtype=torch.uint8, device=dev)
         if scales is None:
             scales = torch.empty((rows_capacity, max(H // 128, 1)), dtype=torch.float32, device=dev)
-        _dev(out, "out", torch.uint8)
-        _dev(scales, "scales", torch.float32)
+        _dev(out, "out", torch.uint8, numel=rows_capacity * H, device=dev)
+        _dev(scales, "scales", torch.float32, numel=rows_capacity * (H // 128), device=dev)
     else:
         if out is None:
             out = torch.empty((rows_capacity, H), dtype=torch.bfloat16, device=dev)
-        _dev(out, "out", torch.bfloat16)
-    if out.numel() < rows_capacity * H:
-        raise ValueError("out holds fewer than rows_capacity rows")
+        _dev(out, "out", torch.bfloat16, numel=rows_capacity * H, device=dev)
     _check("tk_expand_quant", library().tk_expand_quant(
         _ptr(x), T, H, k, _ptr(pos), mode, _ptr(out), _ptr(scales), rows_capacity, _stream(x)))
     return out, scales
@@ -228,15 +238,16 @@ def tk_expand_quant(x: torch.Tensor, pos: torch.Tensor, mode: int, rows_capacity
 def tk_reduce(y: torch.Tensor, pos: torch.Tensor, topk_w: torch.Tensor,
               out: torch.Tensor | None = None):
     _dev(y, "y", torch.bfloat16, 2)
-    _dev(pos, "pos", torch.int32, 2)
-    _dev(topk_w, "topk_w", torch.float32, 2)
+    dev = y.device
+    _dev(pos, "pos", torch.int32, 2, device=dev)
+    _dev(topk_w, "topk_w", torch.float32, 2, device=dev)
     T, k = pos.shape
     R, H = y.shape
     if tuple(topk_w.shape) != (T, k):
         raise ValueError("topk_w must match pos")
     if out is None:
-        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
-    _dev(out, "out", torch.bfloat16, 2)
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _dev(out, "out", torch.bfloat16, 2, T * H, dev)
     _check("tk_reduce", library().tk_reduce(_ptr(y), R, _ptr(pos), _ptr(topk_w), T, k, H,
                                             _ptr(out), _stream(y)))
     return out
@@ -245,12 +256,13 @@ def tk_reduce(y: torch.Tensor, pos: torch.Tensor, topk_w: torch.Tensor,
 def tk_expert_standin(xq: torch.Tensor, scales: torch.Tensor, n_rows: torch.Tensor,
                       mult: float = 0.5, y: torch.Tensor | None = None):
     _dev(xq, "xq", torch.uint8, 2)
-    _dev(scales, "scales", torch.float32, 2)
-    _dev(n_rows, "n_rows", torch.int32)
     cap, H = xq.shape
+    dev = xq.device
+    _dev(scales, "scales", torch.float32, 2, cap * (H // 128), dev)
+    _dev(n_rows, "n_rows", torch.int32, numel=1, device=dev)
     if y is None:
-        y = torch.empty((cap, H), dtype=torch.bfloat16, device=xq.device)
-    _dev(y, "y", torch.bfloat16, 2)
+        y = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
+    _dev(y, "y", torch.bfloat16, 2, cap * H, dev)
     _check("tk_expert_standin", library().tk_expert_standin(
         _ptr(xq), _ptr(scales), _ptr(n_rows), cap, H, float(mult), _ptr(y), _stream(xq)))
     return y
@@ -268,22 +280,23 @@ def tk_swiglu_quant(h: torch.Tensor, n_rows: torch.Tensor | None = None,
     if two_i % 2:
         raise ValueError("h must have 2*I columns")
     I = two_i // 2
+    dev = h.device
     if n_rows is not None:
-        _dev(n_rows, "n_rows", torch.int32)
+        _dev(n_rows, "n_rows", torch.int32, numel=1, device=dev)
     T = k = 0
     if pos is not None:
-        _dev(pos, "pos", torch.int32, 2)
+        _dev(pos, "pos", torch.int32, 2, device=dev)
         T, k = pos.shape
     if row_src is not None:
-        _dev(row_src, "row_src", torch.int32)
+        _dev(row_src, "row_src", torch.int32, numel=cap, device=dev)
     if topk_w is not None:
-        _dev(topk_w, "topk_w", torch.float32)
+        _dev(topk_w, "topk_w", torch.float32, numel=T * k, device=dev)
     if out is None:
-        out = torch.empty((cap, I), dtype=torch.uint8, device=h.device)
+        out = torch.empty((cap, I), dtype=torch.uint8, device=dev)
     if scales is None:
-        scales = torch.empty((cap, max(I // 128, 1)), dtype=torch.float32, device=h.device)
-    _dev(out, "out", torch.uint8)
-    _dev(scales, "scales", torch.float32)
+        scales = torch.empty((cap, max(I // 128, 1)), dtype=torch.float32, device=dev)
+    _dev(out, "out", torch.uint8, numel=cap * I, device=dev)
+    _dev(scales, "scales", torch.float32, numel=cap * (I // 128), device=dev)
     _check("tk_swiglu_quant", library().tk_swiglu_quant(
         _ptr(h), cap, _ptr(n_rows), I, _ptr(row_src), _ptr(pos), _ptr(topk_w), T, k,
         _ptr(out), _ptr(scales), _stream(h)))
@@ -295,19 +308,21 @@ def tk_balance_loss(logits: torch.Tensor, topk_idx: torch.Tensor, score: int,
                     loss: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
     """Per-expert load fraction f, mean normalised score P and loss = sum f*P."""
     _dev(logits, "logits", torch.float32, 2)
-    _dev(topk_idx, "topk_idx", torch.int32, 2)
     T, E = logits.shape
-    k = topk_idx.shape[1]
     dev = logits.device
+    _dev(topk_idx, "topk_idx", torch.int32, 2, device=dev)
+    k = topk_idx.shape[1]
+    if topk_idx.shape[0] != T:
+        raise ValueError("topk_idx must have one row per token")
     f = torch.empty(E, dtype=torch.float32, device=dev) if f is None else f
     P = torch.empty(E, dtype=torch.float32, device=dev) if P is None else P
     loss = torch.empty(1, dtype=torch.float32, device=dev) if loss is None else loss
     need = int(library().tk_balance_workspace_bytes(T, E))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-    for name, t in (("f", f), ("P", P), ("loss", loss)):
-        _dev(t, name, torch.float32)
-    _dev(workspace, "workspace", torch.uint8)
+    for name, t, n in (("f", f, E), ("P", P, E), ("loss", loss, 1)):
+        _dev(t, name, torch.float32, numel=n, device=dev)
+    _dev(workspace, "workspace", torch.uint8, device=dev)
     _check("tk_balance_loss", library().tk_balance_loss(
         _ptr(logits), _ptr(topk_idx), T, E, k, score, _ptr(f), _ptr(P), _ptr(loss),
         _ptr(workspace), workspace.numel(), _stream(logits)))
@@ -339,10 +354,10 @@ def tk_quant(x: torch.Tensor, mode: int, out: torch.Tensor | None = None,
     need = int(library().tk_quant_workspace_bytes(rows, cols, mode))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    _dev(out, "out", torch.uint8)
-    _dev(scales, "scales", torch.float32)
+    _dev(out, "out", torch.uint8, numel=math.prod(oshape), device=x.device)
+    _dev(scales, "scales", torch.float32, numel=math.prod(sshape), device=x.device)
     if workspace is not None:
-        _dev(workspace, "workspace", torch.uint8)
+        _dev(workspace, "workspace", torch.uint8, device=x.device)
     _check("tk_quant", library().tk_quant(_ptr(x), rows, cols, mode, _ptr(out), _ptr(scales),
                                           _ptr(workspace),
                                           0 if workspace is None else workspace.numel(),
@@ -358,23 +373,25 @@ def tk_swiglu_quant_t(h: torch.Tensor, row_src: torch.Tensor | None = None,
     _dev(h, "h", torch.bfloat16, 2)
     rows, two_i = h.shape
     I = two_i // 2
+    dev = h.device
     T = k = 0
     if pos is not None:
-        _dev(pos, "pos", torch.int32, 2)
+        _dev(pos, "pos", torch.int32, 2, device=dev)
         T, k = pos.shape
     if row_src is not None:
-        _dev(row_src, "row_src", torch.int32)
+        _dev(row_src, "row_src", torch.int32, numel=rows, device=dev)
     if topk_w is not None:
-        _dev(topk_w, "topk_w", torch.float32)
-    dev = h.device
+        _dev(topk_w, "topk_w", torch.float32, numel=T * k, device=dev)
     out = torch.empty((rows, I), dtype=torch.uint8, device=dev) if out is None else out
     scales = torch.empty((rows, max(I // 128, 1)), dtype=torch.float32, device=dev) if scales is None else scales
     out_t = torch.empty((I, rows), dtype=torch.uint8, device=dev) if out_t is None else out_t
     scales_t = (torch.empty((I, max(rows // 128, 1)), dtype=torch.float32, device=dev)
                 if scales_t is None else scales_t)
-    for name, t, dt in (("out", out, torch.uint8), ("scales", scales, torch.float32),
-                        ("out_t", out_t, torch.uint8), ("scales_t", scales_t, torch.float32)):
-        _dev(t, name, dt)
+    for name, t, dt, n in (("out", out, torch.uint8, rows * I),
+                           ("scales", scales, torch.float32, rows * (I // 128)),
+                           ("out_t", out_t, torch.uint8, I * rows),
+                           ("scales_t", scales_t, torch.float32, I * (rows // 128))):
+        _dev(t, name, dt, numel=n, device=dev)
     _check("tk_swiglu_quant_t", library().tk_swiglu_quant_t(
         _ptr(h), rows, I, _ptr(row_src), _ptr(pos), _ptr(topk_w), T, k, _ptr(out), _ptr(scales),
         _ptr(out_t), _ptr(scales_t), _stream(h)))
@@ -385,8 +402,6 @@ def tk_silu_bf16(g: torch.Tensor, out=None):
     """RN(g * sigmoid(g)) in fp32 for bf16 g (the SwiGLU kernels' sigmoid lookup)."""
     _dev(g, "g", torch.bfloat16)
     out = torch.empty(g.shape, dtype=torch.float32, device=g.device) if out is None else out
-    _dev(out, "out", torch.float32)
-    if out.numel() != g.numel():
-        raise ValueError("tk_silu_bf16: out must have g's number of elements")
+    _dev(out, "out", torch.float32, numel=g.numel(), device=g.device)
     _check("tk_silu_bf16", library().tk_silu_bf16(_ptr(g), g.numel(), _ptr(out), _stream(g)))
     return out
