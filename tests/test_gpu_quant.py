@@ -104,3 +104,18 @@ def test_quant_zero_rows_and_deterministic():
     e = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
     tk.tk_quant(e, tk.TK_QUANT_FP8_PER_CHANNEL)
     torch.cuda.synchronize()
+
+
+_ALIGN = {tk.TK_QUANT_FP8_1X128: 128, tk.TK_QUANT_FP8_1X128_POW2: 128,
+          tk.TK_QUANT_FP8_128X128: 128, tk.TK_QUANT_FP8_PER_CHANNEL: 8, tk.TK_QUANT_FP4_1X32: 32}
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_quant_sweep(seed):
+    """Seeded random shapes: any mode, 1..600 rows, columns any allowed multiple up to 4096."""
+    rng = np.random.default_rng(7000 + seed)
+    mode = MODES[int(rng.integers(len(MODES)))]
+    a = _ALIGN[mode]
+    rows = int(rng.integers(1, 601))
+    cols = a * int(rng.integers(1, 4096 // a + 1))
+    _check(_matrix(rng, rows, cols), mode)

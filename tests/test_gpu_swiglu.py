@@ -236,3 +236,40 @@ def test_swiglu_quant_t_v3_expert_shape_column_blocks():
         assert np.array_equal(to_host(sc_t[c0:c0 + 128]), st_ref), c0
         bad = np.argwhere(to_host(out_t[c0:c0 + 128]) != qt_ref)
         assert bad.size == 0, f"block {c0}: {len(bad)} transposed codes differ, first {bad[:4]}"
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_swiglu_sweep(seed):
+    """Seeded random shapes for both forms: I any multiple of 128 up to 2048,
+    weighted through a random map or not; the plain form with a device-side
+    row count below its capacity, the transposing form over the map's rows
+    rounded up to whole 128-row blocks (extra rows unweighted: weight 0)."""
+    rng = np.random.default_rng(8000 + seed)
+    I = 128 * int(rng.integers(1, 17))
+    T = int(rng.integers(1, 400))
+    E = int(rng.choice([8, 16, 64]))
+    k = int(rng.integers(1, min(E, 8) + 1))
+    lo = int(rng.integers(0, E))
+    hi = int(rng.integers(lo + 1, E + 1))
+    pos, row_src, w, R = _map(rng, T, E, k, lo, hi)
+    weighted = bool(rng.integers(0, 2))
+    # plain form
+    cap = R + int(rng.integers(0, 40)) + 1
+    h = _rows(rng, cap, I, gscale=float(rng.choice([1.0, 3.0, 8.0])))
+    rs = np.full(cap, -1, np.int32)
+    rs[:R] = row_src
+    n_rows = torch.tensor([R], dtype=torch.int32, device="cuda")
+    args = (to_dev(rs), to_dev(pos), to_dev(w)) if weighted else (None, None, None)
+    q, s = tk.tk_swiglu_quant(to_dev(h, bf16=True), n_rows, *args)
+    torch.cuda.synchronize()
+    rw = oracle.row_weights(pos, w, cap) if weighted else None
+    _check(h, I, to_host(q), to_host(s), R, rw)
+    # transposing form
+    Rt = max(128, (R + 127) // 128 * 128)
+    ht = _rows(rng, Rt, I)
+    rst = np.full(Rt, -1, np.int32)
+    rst[:R] = row_src
+    args = (to_dev(rst), to_dev(pos), to_dev(w)) if weighted else (None, None, None)
+    res = tk.tk_swiglu_quant_t(to_dev(ht, bf16=True), *args)
+    torch.cuda.synchronize()
+    _check_t(ht, I, res, oracle.row_weights(pos, w, Rt) if weighted else None)
