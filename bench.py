@@ -25,8 +25,9 @@ routing path (next_rows) are timed separately on the same data and do not
 enter value: SwiGLU + 1x128 FP8 quantisation of the 65536 expanded rows at
 the DeepSeek-V3 expert width I = 2048 (plain and transposing), weighted by the
 routing weights through the step's map; the padded map; the balance loss;
-the other quantisation granularities of the hidden states; and the expand
-without quantisation (bf16 rows).
+the other quantisation granularities of the hidden states; the expand without
+quantisation (bf16 rows); and one GPU's share of an expert-parallel step
+(T = 32768, experts 32..63 local, with the stand-in expert).
 """
 from __future__ import annotations
 
@@ -272,6 +273,88 @@ def bench_expand_bf16(tk, torch, x, pos, steps):
                                          "algorithmic_bytes": nbytes}}}
 
 
+def bench_ep_share(tk, torch, np, synth, dev, steps):
+    """The one-GPU share of an expert-parallel step: DeepSeek-V3 routing over
+    T = 32768 tokens with experts 32..63 local (a log-Zipf popularity offset on
+    the logits), the map with the local mask, the FP8 expand of the local
+    routes, the stand-in expert (dequantise x 0.5) and the combine of the local
+    routes.  The time includes the stand-in; the bytes leave it out and count x
+    only for the tokens with at least one local route."""
+    cfg = synth.ep_share(0)
+    T4, E4, K4, H4 = cfg["T"], cfg["E"], cfg["k"], cfg["H"]
+    lo, hi = cfg["local"]
+    nl = hi - lo
+    logits = torch.from_numpy(cfg["logits"]).to(dev)
+    x = torch.from_numpy(cfg["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+    del cfg["x"]
+    opts = tk.RouteOpts(**cfg["route"])
+    cap = T4 * K4                               # every route local, at worst
+    idx = torch.empty((T4, K4), dtype=torch.int32, device=dev)
+    w = torch.empty((T4, K4), dtype=torch.float32, device=dev)
+    counts = torch.empty(nl, dtype=torch.int32, device=dev)
+    offsets = torch.empty(nl + 1, dtype=torch.int32, device=dev)
+    pos = torch.empty((T4, K4), dtype=torch.int32, device=dev)
+    row_src = torch.empty(cap, dtype=torch.int32, device=dev)
+    ws = torch.empty(max(tk.tk_map_workspace_bytes(T4, K4, nl), 16), dtype=torch.uint8, device=dev)
+    xq = torch.empty((cap, H4), dtype=torch.uint8, device=dev)
+    sc = torch.empty((cap, H4 // 128), dtype=torch.float32, device=dev)
+    y = torch.empty((cap, H4), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T4, H4), dtype=torch.bfloat16, device=dev)
+
+    names = ("route", "map", "expand", "standin", "reduce")
+
+    def step(ev=None):
+        calls = (lambda: tk.tk_route(logits, None, K4, opts, idx, w),
+                 lambda: tk.tk_map(idx, E4, lo, hi, counts, offsets, pos, row_src, ws),
+                 lambda: tk.tk_expand_quant(x, pos, tk.TK_EXPAND_FP8_E4M3_1X128, cap, xq, sc),
+                 lambda: tk.tk_expert_standin(xq, sc, offsets[nl:], 0.5, y),
+                 lambda: tk.tk_reduce(y, pos, w, out))
+        for i, c in enumerate(calls):
+            if ev is not None:
+                ev[i].record()
+            c()
+        if ev is not None:
+            ev[len(calls)].record()
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    n = min(steps, 20)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(n):
+        step()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / n
+    per = {m: [] for m in names}
+    for _ in range(n):                          # breakdown: an event between calls
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+        step(ev)
+        torch.cuda.synchronize()
+        for i, m in enumerate(names):
+            per[m].append(ev[i].elapsed_time(ev[i + 1]) * 1e3)
+    kern = {m: round(float(np.median(v)), 2) for m, v in per.items()}
+    r_loc = int(offsets[nl].item())
+    t_act = int((pos >= 0).any(dim=1).sum().item())
+    nbytes = (T4 * E4 * 4 + T4 * K4 * 8                                   # route
+              + T4 * K4 * 8 + r_loc * 4 + (2 * nl + 1) * 4                # map
+              + t_act * H4 * 2 + r_loc * H4 + r_loc * (H4 // 128) * 4 + T4 * K4 * 4   # expand
+              + r_loc * H4 * 2 + T4 * K4 * 8 + T4 * H4 * 2)               # reduce
+    return {"ep_share_T32768": {
+        "workload": f"T={T4} H={H4} E={E4} k={K4}, experts [{lo}, {hi}) local; route, masked map, "
+                    "FP8 expand, stand-in expert, combine",
+        "us_per_step": round(us, 2), "timing": "back-to-back steps between two events",
+        "rows_local": r_loc, "tokens_with_local_routes": t_act,
+        "algorithmic_bytes_without_standin": nbytes,
+        "hbm_gbps": round(nbytes / us / 1e3, 1),
+        "hbm_frac": round(nbytes / us / 1e3 / PEAK_HBM_GBPS, 4),
+        "kernel_us_median": kern,
+        "hbm_frac_without_standin_time": round(
+            nbytes / (us - kern["standin"]) / 1e3 / PEAK_HBM_GBPS, 4)}}
+
+
 def bench_quant(tk, torch, x, steps):
     """Each codec granularity on the step's hidden states (8192 x 7168 bf16)."""
     out = {}
@@ -431,7 +514,8 @@ def main() -> int:
                                                   args.steps),
                  **bench_map_balance(tk, torch, logits, idx, args.steps),
                  **bench_quant(tk, torch, x, args.steps),
-                 **bench_expand_bf16(tk, torch, x, pos, args.steps)}
+                 **bench_expand_bf16(tk, torch, x, pos, args.steps),
+                 **bench_ep_share(tk, torch, np, synth, dev, args.steps)}
 
     ms_per_step = total_ms / args.steps
     value = T / (ms_per_step * 1e-3)

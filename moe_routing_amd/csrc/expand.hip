@@ -11,12 +11,15 @@
 // the block amax is a 3-step DPP butterfly inside the group.  The token is
 // read once, quantised once, and its 16 code bytes per lane are stored to
 // each of its k rows (one 1 KiB contiguous segment per row per wave), so HBM
-// traffic is T*H*2 read + R*H written, not R*H*2 read.  The expanded rows are
-// written once and not read again by this pipeline, so they go out through
-// nontemporal stores; the token is read with ordinary loads (on MI355X the
-// nontemporal hint on these reads measured slower).  All scale writes of a
-// row come from one workgroup, so no 4-byte scale shares a cache line with
-// another workgroup's.
+// traffic is T*H*2 read + R*H written, not R*H*2 read; a token none of whose
+// routes has a row (no local expert, or rows beyond the capacity) is not read
+// at all.  The expanded rows are written once and not read again by this
+// pipeline, so they go out through nontemporal stores.  The token is read
+// with ordinary loads, which allocate it in the memory-side cache (MALL,
+// 256 MB): a following pass over the same hidden states finds them there,
+// where a nontemporal read would not.  All scale writes of a row come from
+// one workgroup, so no 4-byte scale shares a cache line with another
+// workgroup's.
 
 // Quotient x/scale: Markstein's correction on the reciprocal,
 //   inv = RN(1/scale); q0 = RN(x*inv); r = fma(-q0, scale, x); q = fma(r, inv, q0)
@@ -46,6 +49,17 @@ __device__ __forceinline__ void token_rows(const int32_t* __restrict__ pos, int 
     for (int j = 0; j < KMAX; ++j) rows[j] = (r[j] >= 0 && r[j] < cap) ? r[j] : -1;
 }
 
+// Whether any of the token's rows is written (the same for every thread of
+// the workgroup, so an early return is uniform).
+template <int KMAX>
+__device__ __forceinline__ bool any_row(const int64_t (&rows)[KMAX])
+{
+    bool any = false;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) any = any || rows[j] >= 0;
+    return any;
+}
+
 // One token per workgroup; K > 0 is a compile-time k, K == 0 a runtime k.
 template <int K>
 __global__ __launch_bounds__(tk::kWave * kExpandWaves) void expand_fp8_kernel(
@@ -61,6 +75,7 @@ __global__ __launch_bounds__(tk::kWave * kExpandWaves) void expand_fp8_kernel(
     const int nb = H / 128;
     int64_t rows[KMAX];
     token_rows<KMAX>(pos, t, k, cap, rows);
+    if (!any_row<KMAX>(rows)) return;   // no destination (e.g. no local route): x is not read
     const uint16_t* xt = x + static_cast<size_t>(t) * H;
     for (int col = wave * kChunkFp8 + lane * 16; col - lane * 16 < H; col += kExpandWaves * kChunkFp8) {
         // H % 128 == 0: an 8-lane group (128 columns) is wholly inside or outside the row
@@ -116,6 +131,7 @@ __global__ __launch_bounds__(tk::kWave * kExpandWaves) void expand_bf16_kernel(
     if (t >= T) return;
     int64_t rows[KMAX];
     token_rows<KMAX>(pos, t, k, cap, rows);
+    if (!any_row<KMAX>(rows)) return;
     const uint16_t* xt = x + static_cast<size_t>(t) * H;
     for (int col = wave * kChunkBf16 + lane * 8; col < H; col += kExpandWaves * kChunkBf16) {
         const tk::u32x4 a = tk::load16(xt + col);
