@@ -113,17 +113,20 @@ def cpu_baseline(inputs, reps: int = 2) -> dict:
         t_ex += t2 - t1
         t_rd += t3 - t2
     secs = (t_rm + t_ex + t_rd) / reps
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), model)
+    except OSError:
+        pass
     return {"value": round(T / secs, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "host": f"{model}, {os.cpu_count()} logical CPUs visible",
             "sample": f"{reps} full steps (T={T} each) of route+map+expand(FP8)+reduce through the "
                       f"single-threaded C oracle, mean per step: route+map {t_rm / reps:.2f}s, "
                       f"expand {t_ex / reps:.2f}s, reduce {t_rd / reps:.2f}s"}
 
 
-# SwiGLU + FP8 row: the defined arithmetic per output element, one IEEE fp32
-# operation per rounding: sigmoid 17 (negate, two range tests, y*log2e, rint,
-# two Cody-Waite fmas, seven Horner fmas, ldexp, 1+E, division), g*s, *u, *w,
-# |a|, block max, quotient, E4M3 encode.
-SWIGLU_I = 2048
+SWIGLU_I = 2048   # DeepSeek-V3's expert width
 
 
 def bench_swiglu(tk, torch, y, n_rows, row_src, pos, w, steps):
