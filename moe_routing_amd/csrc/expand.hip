@@ -32,6 +32,8 @@
 
 namespace {
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 constexpr int kChunkFp8 = 1024;   // columns per wave step, FP8 mode (16 per lane)
 constexpr int kChunkBf16 = 512;   // columns per wave step, bf16 mode (8 per lane)
 constexpr int kExpandWaves = 8;   // waves per workgroup (one token per workgroup)
@@ -156,25 +158,47 @@ __global__ __launch_bounds__(tk::kBlock) void standin_kernel(
                      tk::uniform(threadIdx.x / tk::kWave);
          u < n_units; u += stride) {
         const int64_t r = u / chunks;
-        const int col = static_cast<int>(u - r * chunks) * kChunkFp8 + lane * 16;
-        if (col >= H) continue;
-        const uint4 q = *reinterpret_cast<const uint4*>(xq + static_cast<size_t>(r) * H + col);
-        const float sc = scales[static_cast<size_t>(r) * nb + col / 128];
-        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-        uint32_t o[8];
+        const int c0 = static_cast<int>(u - r * chunks) * kChunkFp8 + lane * 8;
+        const uint8_t* xr = xq + static_cast<size_t>(r) * H;
+        const float* sr = scales + static_cast<size_t>(r) * nb;
+        uint16_t* yr = y + static_cast<size_t>(r) * H;
+        // lane l takes 8 columns at l*8 and 8 more at 512 + l*8: every load
+        // and store instruction covers one contiguous run (512 B of codes,
+        // 1 KiB of bf16), so streaming stores leave as whole lines.  y is
+        // read once, by the combine: plain stores would leave it dirty in the
+        // memory-side cache and the combine's own writes would pay for its
+        // write-back.
+        // both halves' loads go out before any arithmetic; a lane past the
+        // row's end (H % 128 == 0: 16-lane groups are wholly in or out) reads
+        // column 0 and stores nothing
+        int col[2];
+        bool in[2];
+        u32x2 q[2];
+        float sc[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int wi = static_cast<int>(w[i]);
-            const float d0 = __builtin_amdgcn_cvt_f32_fp8(wi, 0);
-            const float d1 = __builtin_amdgcn_cvt_f32_fp8(wi, 1);
-            const float d2 = __builtin_amdgcn_cvt_f32_fp8(wi, 2);
-            const float d3 = __builtin_amdgcn_cvt_f32_fp8(wi, 3);
-            o[2 * i] = tk::pack_bf16x2((d0 * sc) * mult, (d1 * sc) * mult);
-            o[2 * i + 1] = tk::pack_bf16x2((d2 * sc) * mult, (d3 * sc) * mult);
+        for (int half = 0; half < 2; ++half) {
+            col[half] = c0 + half * (kChunkFp8 / 2);
+            in[half] = col[half] < H;
+            const int cl = in[half] ? col[half] : 0;
+            q[half] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(xr + cl));
+            sc[half] = sr[cl / 128];
         }
-        uint4* dst = reinterpret_cast<uint4*>(y + static_cast<size_t>(r) * H + col);
-        dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-        dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const uint32_t w[2] = {q[half].x, q[half].y};
+            uint32_t o[4];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int wi = static_cast<int>(w[i]);
+                const float d0 = __builtin_amdgcn_cvt_f32_fp8(wi, 0);
+                const float d1 = __builtin_amdgcn_cvt_f32_fp8(wi, 1);
+                const float d2 = __builtin_amdgcn_cvt_f32_fp8(wi, 2);
+                const float d3 = __builtin_amdgcn_cvt_f32_fp8(wi, 3);
+                o[2 * i] = tk::pack_bf16x2((d0 * sc[half]) * mult, (d1 * sc[half]) * mult);
+                o[2 * i + 1] = tk::pack_bf16x2((d2 * sc[half]) * mult, (d3 * sc[half]) * mult);
+            }
+            if (in[half]) tk::store_stream(yr + col[half], tk::u32x4{o[0], o[1], o[2], o[3]});
+        }
     }
 }
 

@@ -197,6 +197,21 @@ def test_reduce_random(T, E, k, H):
     _check_reduce(y, pos, w)
 
 
+@pytest.mark.parametrize("T", [1, 2, 3, 5])
+@pytest.mark.parametrize("k", [1, 4, 8])
+def test_reduce_few_tokens(T, k):
+    # a handful of tokens: fewer waves than the grid's first workgroup row,
+    # odd counts, k of one slot and of the compiled sizes
+    H = 1032
+    rng = np.random.default_rng(100 * T + k)
+    R = T * k
+    pos = rng.permutation(R).astype(np.int32).reshape(T, k)
+    pos[rng.random((T, k)) < 0.25] = -1      # some masked slots
+    y = synth.normal_bf16(rng, (R, H))
+    w = rng.random((T, k)).astype(np.float32)
+    _check_reduce(y, pos, w)
+
+
 def test_reduce_masked_and_empty_tokens():
     T, E, k, H = 400, 64, 8, 1024
     idx, pos, R = _routing(T, E, k, 31, lo=32, hi=40)
