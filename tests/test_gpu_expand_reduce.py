@@ -80,7 +80,7 @@ def _check_expand_fp8(x_bits, pos, R):
 
 
 @pytest.mark.parametrize("T,E,k,H", [(64, 16, 2, 256), (100, 32, 3, 1152), (513, 64, 8, 7168),
-                                     (37, 8, 1, 128), (200, 16, 4, 3072)])
+                                     (37, 8, 1, 128), (200, 16, 4, 3072), (60, 64, 32, 1024)])
 def test_expand_fp8_random(T, E, k, H):
     idx, pos, R = _routing(T, E, k, T + H)
     rng = np.random.default_rng(H)
@@ -142,7 +142,7 @@ def test_expand_skips_and_capacity():
 
 
 @pytest.mark.parametrize("T,E,k,H", [(64, 16, 2, 256), (129, 8, 3, 520), (10, 4, 1, 8),
-                                     (300, 64, 8, 7168)])
+                                     (300, 64, 8, 7168), (50, 64, 32, 512)])
 def test_expand_bf16(T, E, k, H):
     idx, pos, R = _routing(T, E, k, T * 3 + H)
     x = synth.normal_bf16(np.random.default_rng(T), (T, H))
@@ -188,7 +188,7 @@ def _check_reduce(y_bits, pos, w, sample=None):
 
 
 @pytest.mark.parametrize("T,E,k,H", [(64, 16, 2, 256), (333, 32, 8, 1032), (50, 8, 1, 128),
-                                     (77, 64, 6, 7168), (40, 64, 12, 512)])
+                                     (77, 64, 6, 7168), (40, 64, 12, 512), (45, 64, 32, 1032)])
 def test_reduce_random(T, E, k, H):
     idx, pos, R = _routing(T, E, k, T + k)
     rng = np.random.default_rng(H + k)

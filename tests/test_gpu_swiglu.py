@@ -49,7 +49,8 @@ def test_swiglu_quant_random(R, I):
 
 
 @pytest.mark.parametrize("T,E,k,lo,hi,I", [(300, 32, 4, 0, 32, 256), (500, 64, 8, 16, 48, 1152),
-                                          (129, 16, 2, 0, 16, 2048)])
+                                          (129, 16, 2, 0, 16, 2048), (96, 64, 32, 0, 64, 256),
+                                          (150, 32, 12, 8, 30, 384)])
 def test_swiglu_quant_weighted_by_map(T, E, k, lo, hi, I):
     rng = np.random.default_rng(T + E + I)
     pos, row_src, w, R = _map(rng, T, E, k, lo, hi)
@@ -143,11 +144,13 @@ def test_swiglu_quant_t_random(R, I):
     _check_t(h, I, res)
 
 
-def test_swiglu_quant_t_weighted_aligned_map():
+@pytest.mark.parametrize("T,E,k", [(400, 16, 4), (150, 32, 12), (60, 64, 32)])
+def test_swiglu_quant_t_weighted_aligned_map(T, E, k):
     """Rows laid out by the aligned map (segments padded to 128 rows), weights
-    through row_src / pos; padding rows have weight 0."""
-    rng = np.random.default_rng(83)
-    T, E, k, I = 400, 16, 4, 256
+    through row_src / pos; padding rows have weight 0.  k above 8 takes the
+    kernel's extra slot loop."""
+    rng = np.random.default_rng(83 + k)
+    I = 256
     idx = synth.random_routing(rng, T, E, k)
     _, offsets, pos, row_src = oracle.map_aligned(idx, E, 0, E, 128)
     R = int(offsets[-1])
