@@ -71,6 +71,9 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // kQuadXor1 / kQuadXor2: quad_perm [1,0,3,2] / [2,3,0,1]; kHalfMirror: lane
 // i <-> 7-i within 8 lanes; kMirror: lane i <-> 15-i within 16 lanes.
 constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kHalfMirror = 0x141, kMirror = 0x140;
+// Across rows (GFX9 DPP): lane 15 of each row to the whole next row, and lane
+// 31 to rows 2 and 3; which rows are written is the instruction's row mask.
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
 
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
@@ -116,9 +119,15 @@ __device__ __forceinline__ uint32_t max_wave_u32(uint32_t v)
     v = max(v, dpp_u32<kQuadXor2>(v));
     v = max(v, dpp_u32<kHalfMirror>(v));
     v = max(v, dpp_u32<kMirror>(v));
-    const uint32_t r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31);
-    const uint32_t r2 = __builtin_amdgcn_readlane(v, 47), r3 = __builtin_amdgcn_readlane(v, 63);
-    return max(max(r0, r1), max(r2, r3));
+    // every lane of a row now holds the row's maximum.  row_bcast:15 brings
+    // lane 15 of rows 0 and 2 into rows 1 and 3, row_bcast:31 lane 31 into
+    // rows 2 and 3 (rows outside the row mask keep their value, as max with
+    // 0 leaves it), so lane 63 holds the maximum of all four rows
+    v = max(v, static_cast<uint32_t>(
+                   __builtin_amdgcn_update_dpp(0, static_cast<int>(v), kRowBcast15, 0xA, 0xF, false)));
+    v = max(v, static_cast<uint32_t>(
+                   __builtin_amdgcn_update_dpp(0, static_cast<int>(v), kRowBcast31, 0xC, 0xF, false)));
+    return __builtin_amdgcn_readlane(v, 63);
 }
 
 // Sum / maximum over the whole wave, returned wave-uniform.  DPP row steps
