@@ -7,18 +7,20 @@
 // token per thread.  Two launches at the usual sizes, no atomics on global
 // memory, so every output is a pure function of topk_idx:
 //   1. count  one workgroup per tile: LDS histogram of the tile's local
-//             routes -> cnt[e][tile] (expert-major) in the workspace
+//             routes -> cnt[tile][e] (tile-major: each tile writes whole
+//             lines of its own) in the workspace
 //   2. place  one workgroup per tile: per expert, the sum over all tiles
 //             (total) and over the tiles before this one (before); a block
 //             scan of the totals gives offsets; then a bit mask per
 //             (expert, sub-tile) in LDS ranks the tile's tokens:
 //               pos = offsets[e] + before[e] + (tokens of e in earlier
 //                     sub-tiles) + popcount(bits below t in t's sub-tile)
-// The place kernel issues all its global loads (its tokens' ids, the count
-// rows) before any of the dependent work, so their latencies overlap.  When
-// the count matrix is large, a third launch (scan, between the two) turns the
-// counts into per-tile prefixes once, so that place reads one column instead
-// of a whole row per expert.
+// The place kernel issues its global loads (its tokens' ids, then its
+// experts' count columns, 32 tiles per batch, coalesced across the threads
+// that own neighbouring experts) before waiting on any of them, so their
+// latencies overlap.  When the count matrix is large, a third launch (scan,
+// between the two) turns the counts into per-tile prefixes once, so that
+// place reads one entry instead of a whole column per expert.
 // Ranks follow token order, which is the stable order because a token is
 // routed to an expert at most once (repeats in a row are dropped).
 // tk_map_aligned pads every expert's segment to a multiple of `align` rows
@@ -33,12 +35,12 @@ constexpr int kMaxSub = kThreads / kSub;  // one token per thread: tiles <= 256 
 constexpr int kMaxFusedInts = 32768;   // count matrix read whole by each place workgroup
 constexpr int kLdsWords = 12288;       // place kernel LDS budget (48 KiB)
 constexpr int kScanThreads = 1024;
+constexpr int kBatch = 32;             // count loads in flight per thread (place, scan)
 
 struct Tiling {
     int S;          // sub-tiles per tile
     int tile;       // tokens per tile
     int n_tiles;
-    int pitch;      // ints per expert row of cnt (n_tiles rounded up to 4)
     bool fused;     // place computes prefixes itself
 };
 
@@ -51,21 +53,27 @@ __host__ inline Tiling tiling(int T, int n_local)
     g.S = s < 1 ? 1 : (s > s_max ? s_max : s);
     g.tile = g.S * kSub;
     g.n_tiles = T > 0 ? (T + g.tile - 1) / g.tile : 0;
-    g.pitch = (g.n_tiles + 3) & ~3;
-    g.fused = static_cast<int64_t>(g.pitch) * n_local <= kMaxFusedInts;
+    g.fused = static_cast<int64_t>(g.n_tiles) * n_local <= kMaxFusedInts;
     return g;
 }
 
-// Token t's k expert ids as local indices (id - lo); -1 for an id outside
-// [lo, hi) and for a repeat of an id earlier in the row.
+// Token t's k expert ids as stored (loads only, so that a caller can issue
+// more loads before the first use); -1 past k.
 template <int KMAX>
-__device__ __forceinline__ void load_local_ids(const int32_t* __restrict__ idx, int t, int k,
-                                               int lo, int hi, int (&e)[KMAX])
+__device__ __forceinline__ void load_raw_ids(const int32_t* __restrict__ idx, int t, int k,
+                                             int (&raw)[KMAX])
 {
     const int32_t* r = idx + static_cast<size_t>(t) * k;
-    int raw[KMAX];
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) raw[j] = (j < k) ? r[j] : -1;
+}
+
+// Stored ids -> local indices (id - lo); -1 for an id outside [lo, hi) and
+// for a repeat of an id earlier in the row.
+template <int KMAX>
+__device__ __forceinline__ void local_ids(const int (&raw)[KMAX], int k, int lo, int hi,
+                                          int (&e)[KMAX])
+{
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
         bool keep = (j < k) && raw[j] >= lo && raw[j] < hi;
@@ -76,8 +84,17 @@ __device__ __forceinline__ void load_local_ids(const int32_t* __restrict__ idx, 
 }
 
 template <int KMAX>
+__device__ __forceinline__ void load_local_ids(const int32_t* __restrict__ idx, int t, int k,
+                                               int lo, int hi, int (&e)[KMAX])
+{
+    int raw[KMAX];
+    load_raw_ids<KMAX>(idx, t, k, raw);
+    local_ids<KMAX>(raw, k, lo, hi, e);
+}
+
+template <int KMAX>
 __global__ __launch_bounds__(kThreads) void map_count_kernel(
-    const int32_t* __restrict__ idx, int T, int k, int lo, int hi, int tile_tokens, int pitch,
+    const int32_t* __restrict__ idx, int T, int k, int lo, int hi, int tile_tokens,
     int32_t* __restrict__ cnt)
 {
     extern __shared__ int32_t hist[];
@@ -95,28 +112,27 @@ __global__ __launch_bounds__(kThreads) void map_count_kernel(
     }
     __syncthreads();
     for (int i = threadIdx.x; i < nl; i += kThreads)
-        cnt[static_cast<size_t>(i) * pitch + blockIdx.x] = hist[i];
-    // the padding columns [n_tiles, pitch) of every row are read as part of
-    // whole int4s later: the first tile writes them as zeros
-    if (blockIdx.x == 0) {
-        for (int i = threadIdx.x; i < nl; i += kThreads)
-            for (int c = gridDim.x; c < pitch; ++c) cnt[static_cast<size_t>(i) * pitch + c] = 0;
-    }
+        cnt[static_cast<size_t>(blockIdx.x) * nl + i] = hist[i];
 }
 
-// Many tiles: cnt[e][tile] -> exclusive prefix over tiles (in place), and
-// totals[e] = the sum over all tiles.  One workgroup, a thread per expert.
+// Many tiles: cnt[tile][e] -> exclusive prefix over tiles (in place), and
+// totals[e] = the sum over all tiles.  One workgroup, a thread per expert;
+// each batch of kBatch tiles is loaded before any of it is rewritten.
 __global__ __launch_bounds__(kScanThreads) void map_scan_kernel(
-    int32_t* __restrict__ cnt, int n_tiles, int pitch, int nl, int32_t* __restrict__ totals)
+    int32_t* __restrict__ cnt, int n_tiles, int nl, int32_t* __restrict__ totals)
 {
     for (int e = threadIdx.x; e < nl; e += kScanThreads) {
-        int32_t* row = cnt + static_cast<size_t>(e) * pitch;
         int32_t run = 0;
-        for (int i = 0; i < n_tiles; i += 4) {   // pitch % 4 == 0: whole int4s
-            int4 c = *reinterpret_cast<const int4*>(row + i);
-            const int4 ex = make_int4(run, run + c.x, run + c.x + c.y, run + c.x + c.y + c.z);
-            run += c.x + c.y + c.z + c.w;
-            *reinterpret_cast<int4*>(row + i) = ex;
+        for (int c0 = 0; c0 < n_tiles; c0 += kBatch) {
+            int32_t v[kBatch];
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b)
+                v[b] = (c0 + b < n_tiles) ? cnt[static_cast<size_t>(c0 + b) * nl + e] : 0;
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b) {
+                if (c0 + b < n_tiles) cnt[static_cast<size_t>(c0 + b) * nl + e] = run;
+                run += v[b];
+            }
         }
         totals[e] = run;
     }
@@ -148,8 +164,7 @@ __device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* wave
 
 template <int KMAX>
 __global__ __launch_bounds__(kThreads) void map_place_kernel(
-    const int32_t* __restrict__ idx, int T, int k, int lo, int hi, int S, int n_tiles, int pitch,
-    int fused, int align, const int32_t* __restrict__ cnt, const int32_t* __restrict__ totals,
+    const int32_t* __restrict__ idx, int T, int k, int lo, int hi, int S, int n_tiles, int fused, int align, const int32_t* __restrict__ cnt, const int32_t* __restrict__ totals,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ pos,
     int32_t* __restrict__ row_src)
 {
@@ -165,30 +180,37 @@ __global__ __launch_bounds__(kThreads) void map_place_kernel(
     const int t = tile * tile_tokens + tl;
     const bool mine = tl < tile_tokens && t < T;
 
-    // 0. this thread's token: its local expert ids (loads issued first)
-    int e[KMAX];
-    if (mine) load_local_ids<KMAX>(idx, t, k, lo, hi, e);
+    // 0. this thread's token: its stored expert ids.  Only the loads here:
+    //    the count loads below go out before any of them is waited on.
+    int raw[KMAX];
+    if (mine) load_raw_ids<KMAX>(idx, t, k, raw);
 
     // 1. per expert: total over all tiles, sum over the tiles before this one
-    //    (this thread owns the ept consecutive experts [e0, e0 + ept))
+    //    (this thread owns the ept consecutive experts [e0, e0 + ept)).  A
+    //    column is read kBatch tiles at a time, every load of a batch issued
+    //    before the first is used (up to kBatch tiles is one round trip).
     const int ept = (nl + kThreads - 1) / kThreads;
     const int e0 = threadIdx.x * ept;
     int32_t my_total = 0;
     for (int i = 0; i < ept; ++i) {
         const int ex = e0 + i;
         if (ex >= nl) break;
-        const int32_t* row = cnt + static_cast<size_t>(ex) * pitch;
         int32_t tot = 0, bef = 0;
         if (fused) {
-            for (int c = 0; c < n_tiles; c += 4) {
-                const int4 v = *reinterpret_cast<const int4*>(row + c);
-                tot += v.x + v.y + v.z + v.w;
-                bef += (c < tile ? v.x : 0) + (c + 1 < tile ? v.y : 0) +
-                       (c + 2 < tile ? v.z : 0) + (c + 3 < tile ? v.w : 0);
+            for (int c0 = 0; c0 < n_tiles; c0 += kBatch) {
+                int32_t v[kBatch];
+#pragma unroll
+                for (int b = 0; b < kBatch; ++b)
+                    v[b] = (c0 + b < n_tiles) ? cnt[static_cast<size_t>(c0 + b) * nl + ex] : 0;
+#pragma unroll
+                for (int b = 0; b < kBatch; ++b) {
+                    tot += v[b];
+                    bef += (c0 + b < tile) ? v[b] : 0;
+                }
             }
         } else {
             tot = totals[ex];
-            bef = row[tile];
+            bef = cnt[static_cast<size_t>(tile) * nl + ex];
         }
         base[ex] = bef;
         my_total += (tot + align - 1) / align * align;   // the expert's segment, padded
@@ -196,6 +218,8 @@ __global__ __launch_bounds__(kThreads) void map_place_kernel(
         before_sub[ex] = static_cast<uint32_t>(tot);
     }
     for (int i = threadIdx.x; i < nl * S; i += kThreads) mask[i] = 0;
+    int e[KMAX];
+    if (mine) local_ids<KMAX>(raw, k, lo, hi, e);
     __syncthreads();
 
     // 2. bit masks per (expert, sub-tile); offsets = exclusive scan of the
@@ -224,27 +248,45 @@ __global__ __launch_bounds__(kThreads) void map_place_kernel(
     if (tile == 0 && threadIdx.x == 0) offsets[nl] = grand;
     __syncthreads();
 
-    // 3. tokens of each expert in the earlier sub-tiles of this tile
+    // 3. tokens of each expert in the earlier sub-tiles of this tile (the
+    //    expert's S mask words are read into registers before any prefix is
+    //    written: mask and before_sub share one LDS array)
     for (int ex = threadIdx.x; ex < nl; ex += kThreads) {
+        uint32_t m[kMaxSub];
+#pragma unroll
+        for (int sb = 0; sb < kMaxSub; ++sb)   // clamped index: no branch per read
+            m[sb] = mask[ex * S + (sb < S ? sb : S - 1)];
         uint32_t r = 0;
-        for (int sb = 0; sb < S; ++sb) {
-            before_sub[ex * S + sb] = r;
-            r += __popc(mask[ex * S + sb]);
+#pragma unroll
+        for (int sb = 0; sb < kMaxSub; ++sb) {
+            if (sb < S) before_sub[ex * S + sb] = r;
+            r += __popc(m[sb]);
         }
     }
     __syncthreads();
 
-    // 4. positions
+    // 4. positions: every route's three LDS words are read before any is
+    //    used (a masked route reads expert 0's words and discards them)
     if (!mine) return;
     const uint32_t below = (1u << (tl % kSub)) - 1u;
     const int sb = tl / kSub;
+    int32_t bb[KMAX];
+    uint32_t bs[KMAX], mk[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        if (j >= k) break;
+        const int ee = e[j] >= 0 ? e[j] : 0;
+        const int w = ee * S + sb;
+        bb[j] = base[ee];
+        bs[j] = before_sub[w];
+        mk[j] = mask[w];
+    }
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
         if (j >= k) break;
         int32_t p = -1;
         if (e[j] >= 0) {
-            const int w = e[j] * S + sb;
-            p = base[e[j]] + static_cast<int32_t>(before_sub[w] + __popc(mask[w] & below));
+            p = bb[j] + static_cast<int32_t>(bs[j] + __popc(mk[j] & below));
             if (row_src != nullptr) row_src[p] = t;
         }
         pos[static_cast<size_t>(t) * k + j] = p;
@@ -267,8 +309,8 @@ TK_EXPORT size_t tk_map_workspace_bytes(int32_t T, int32_t k, int32_t n_local)
     (void)k;
     if (T <= 0 || n_local <= 0) return 0;
     const Tiling g = tiling(T, n_local);
-    // cnt[n_local][pitch] + totals[n_local]
-    return (static_cast<size_t>(n_local) * g.pitch + static_cast<size_t>(n_local)) * sizeof(int32_t);
+    // cnt[n_tiles][n_local] + totals[n_local]
+    return (static_cast<size_t>(g.n_tiles) * n_local + static_cast<size_t>(n_local)) * sizeof(int32_t);
 }
 
 TK_EXPORT tk_status tk_map_aligned(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
@@ -312,27 +354,27 @@ TK_EXPORT tk_status tk_map_aligned(const int32_t* topk_idx, int32_t T, int32_t k
     }
     const Tiling g = tiling(T, nl);
     int32_t* cnt = static_cast<int32_t*>(workspace);
-    int32_t* totals = cnt + static_cast<size_t>(nl) * g.pitch;
+    int32_t* totals = cnt + static_cast<size_t>(g.n_tiles) * nl;
     const dim3 grid(g.n_tiles), block(kThreads);
     const bool small_k = k <= 8;
     e = small_k
         ? tk::launch(map_count_kernel<8>, grid, block, nl * sizeof(int32_t), stream, topk_idx, T, k,
-                     local_begin, local_end, g.tile, g.pitch, cnt)
+                     local_begin, local_end, g.tile, cnt)
         : tk::launch(map_count_kernel<TK_MAX_TOPK>, grid, block, nl * sizeof(int32_t), stream,
-                     topk_idx, T, k, local_begin, local_end, g.tile, g.pitch, cnt);
+                     topk_idx, T, k, local_begin, local_end, g.tile, cnt);
     if (e != hipSuccess) return tk::launched(e, "tk_map (count)");
     if (!g.fused) {
-        e = tk::launch(map_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, cnt, g.n_tiles,
-                       g.pitch, nl, totals);
+        e = tk::launch(map_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, cnt, g.n_tiles, nl,
+                       totals);
         if (e != hipSuccess) return tk::launched(e, "tk_map (scan)");
     }
     const size_t lds = (2 * static_cast<size_t>(nl) * g.S + nl) * sizeof(uint32_t);
     e = small_k
         ? tk::launch(map_place_kernel<8>, grid, block, lds, stream, topk_idx, T, k, local_begin,
-                     local_end, g.S, g.n_tiles, g.pitch, g.fused ? 1 : 0, align, cnt, totals,
+                     local_end, g.S, g.n_tiles, g.fused ? 1 : 0, align, cnt, totals,
                      counts, offsets, pos, row_src)
         : tk::launch(map_place_kernel<TK_MAX_TOPK>, grid, block, lds, stream, topk_idx, T, k,
-                     local_begin, local_end, g.S, g.n_tiles, g.pitch, g.fused ? 1 : 0, align, cnt,
+                     local_begin, local_end, g.S, g.n_tiles, g.fused ? 1 : 0, align, cnt,
                      totals, counts, offsets, pos, row_src);
     return tk::launched(e, "tk_map (place)");
 }

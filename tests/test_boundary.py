@@ -123,13 +123,13 @@ def test_map_rejects_bad_arguments(lib):
 
 
 def test_map_workspace_bytes(lib):
-    # per-tile counts, one row of `pitch` ints per local expert (pitch = tiles
-    # rounded up to 4), plus one int per local expert
+    # per-tile counts, one row of n_local ints per tile, plus one int per
+    # local expert
     f = lib.tk_map_workspace_bytes
     assert f(0, 8, 256) == 0
-    assert f(8192, 8, 256) == (256 * 32 + 256) * 4     # 32 tiles of 256 tokens
-    assert f(32768, 8, 32) == (32 * 128 + 32) * 4      # 128 tiles of 256 tokens
-    assert f(1, 1, 1024) == (1024 * 4 + 1024) * 4      # one tile, pitch 4
+    assert f(8192, 8, 256) == (32 * 256 + 256) * 4     # 32 tiles of 256 tokens
+    assert f(32768, 8, 32) == (128 * 32 + 32) * 4      # 128 tiles of 256 tokens
+    assert f(1, 1, 1024) == (1 * 1024 + 1024) * 4      # one tile
 
 
 def _expand(lib, T, H, k, mode, cap, x=FAKE, out=FAKE, scales=FAKE, pos=FAKE):
