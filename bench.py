@@ -20,7 +20,8 @@ pipeline's algorithmic HBM GB/s, per-kernel times from HIP events recorded on
 the launch stream (mean, median, p10, p90), the same step with the MALL and
 L2 evicted before each pass (cold_cache), the rate of the repository's
 streaming copy kernel for reference (stream_copy), the roofline of the
-dominant kernel (the reduce) and the CPU oracle's rate.  Steps beyond the
+dominant kernel (the reduce) and the CPU oracle's rate (one thread, and
+all host cores on token shards).  Steps beyond the
 routing path (next_rows) are timed separately on the same data and do not
 enter value: SwiGLU + 1x128 FP8 quantisation of the 65536 expanded rows at
 the DeepSeek-V3 expert width I = 2048 (plain and transposing), weighted by the
@@ -94,7 +95,15 @@ def measured_traffic():
 
 
 def cpu_baseline(inputs, reps: int = 2) -> dict:
-    """The oracle, as it stands, on full steps of the workload, one thread."""
+    """The oracle, as it stands, on full steps of the workload: one thread,
+    then all host cores (at most 16).  The all-cores leg calls the same oracle
+    functions on token shards from a thread pool -- route, expand and reduce
+    are independent per token, and ctypes releases the interpreter lock
+    around each C call -- with the map run serially; its outputs are checked
+    equal to the one-thread run's."""
+    import ctypes
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
     import oracle
     logits, bias, x, y, r = inputs
@@ -108,7 +117,6 @@ def cpu_baseline(inputs, reps: int = 2) -> dict:
         t2 = time.perf_counter()
         out = oracle.reduce(y, pos, w.astype(np.float32))
         t3 = time.perf_counter()
-        del xq, sc, out
         t_rm += t1 - t0
         t_ex += t2 - t1
         t_rd += t3 - t2
@@ -119,11 +127,51 @@ def cpu_baseline(inputs, reps: int = 2) -> dict:
             model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), model)
     except OSError:
         pass
+
+    n = max(1, min(16, os.cpu_count() or 1))
+    shards = [(T * i // n, T * (i + 1) // n) for i in range(n)]
+    L = oracle.lib()
+    xs = np.ascontiguousarray(x)
+    xq_m = np.zeros((R, H), np.uint8)
+    sc_m = np.zeros((R, NB), np.float32)
+    ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    m_rm = m_ex = m_rd = 0.0
+    with ThreadPoolExecutor(n) as ex:
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            parts = list(ex.map(lambda s: oracle.route(logits[s[0]:s[1]], bias, K, **r), shards))
+            idx_m = np.concatenate([p[0] for p in parts])
+            w_m = np.concatenate([p[1] for p in parts])
+            _, _, pos_m, _ = oracle.map_routes(idx_m, E)
+            t1 = time.perf_counter()
+
+            def expand_shard(s):
+                rc = L.orc_expand(ptr(xs[s[0]:]), s[1] - s[0], H, K, ptr(pos_m[s[0]:]), 1, R,
+                                  ptr(xq_m), ptr(sc_m))
+                assert rc == 0
+            list(ex.map(expand_shard, shards))
+            t2 = time.perf_counter()
+            w32 = w_m.astype(np.float32)
+            out_m = np.concatenate(list(ex.map(
+                lambda s: oracle.reduce(y, pos_m[s[0]:s[1]], w32[s[0]:s[1]]), shards)))
+            t3 = time.perf_counter()
+            m_rm += t1 - t0
+            m_ex += t2 - t1
+            m_rd += t3 - t2
+    same = bool(np.array_equal(idx_m, idx) and np.array_equal(w_m, w) and np.array_equal(pos_m, pos)
+                and np.array_equal(xq_m, xq) and np.array_equal(sc_m, sc) and np.array_equal(out_m, out))
+    m_secs = (m_rm + m_ex + m_rd) / reps
     return {"value": round(T / secs, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "host": f"{model}, {os.cpu_count()} logical CPUs visible",
             "sample": f"{reps} full steps (T={T} each) of route+map+expand(FP8)+reduce through the "
                       f"single-threaded C oracle, mean per step: route+map {t_rm / reps:.2f}s, "
-                      f"expand {t_ex / reps:.2f}s, reduce {t_rd / reps:.2f}s"}
+                      f"expand {t_ex / reps:.2f}s, reduce {t_rd / reps:.2f}s",
+            "all_cores": {"value": round(T / m_secs, 1), "unit": "tokens/s", "cores": n,
+                          "kind": "oracle", "identical_to_one_thread": same,
+                          "sample": f"the same {reps} steps, the oracle's route, expand and reduce "
+                                    f"on {n} token shards in {n} threads, map serial; mean per "
+                                    f"step: route+map {m_rm / reps:.2f}s, expand {m_ex / reps:.2f}s, "
+                                    f"reduce {m_rd / reps:.2f}s"}}
 
 
 SWIGLU_I = 2048   # DeepSeek-V3's expert width
