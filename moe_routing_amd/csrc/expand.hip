@@ -5,8 +5,8 @@
 // shape, "剛剛，DeepSeek開始頻繁更新：Tile Kernels、DeepEP V2", section 性能表現).
 // Also tk_expert_standin, the dequantise-and-scale harness kernel.
 //
-// Token-major: one workgroup of 8 waves per token.  Wave w walks the row's
-// 1024-column chunks w, w+8, ...; each lane reads 16 bf16 (two 16-byte
+// Token-major: one workgroup of 4 waves per token.  Wave w walks the row's
+// 1024-column chunks w, w+4, ...; each lane reads 16 bf16 (two 16-byte
 // loads), so every 8-lane group holds one 128-column quantisation block and
 // the block amax is a 3-step DPP butterfly inside the group.  The token is
 // read once, quantised once, and its 16 code bytes per lane are stored to
@@ -36,7 +36,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kChunkFp8 = 1024;   // columns per wave step, FP8 mode (16 per lane)
 constexpr int kChunkBf16 = 512;   // columns per wave step, bf16 mode (8 per lane)
-constexpr int kExpandWaves = 8;   // waves per workgroup (one token per workgroup)
+constexpr int kExpandWaves = 4;   // waves per workgroup (one token per workgroup; a token
+                                  // with no row costs the dispatcher 4 waves, not 8)
 
 // Rows of token t: rows[j] for j < k, -1 where the route is skipped.
 template <int KMAX>
