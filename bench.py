@@ -27,8 +27,9 @@ enter value: SwiGLU + 1x128 FP8 quantisation of the 65536 expanded rows at
 the DeepSeek-V3 expert width I = 2048 (plain and transposing), weighted by the
 routing weights through the step's map; the padded map; the balance loss;
 the other quantisation granularities of the hidden states; the expand without
-quantisation (bf16 rows); and one GPU's share of an expert-parallel step
-(T = 32768, experts 32..63 local, with the stand-in expert).
+quantisation (bf16 rows); one GPU's share of an expert-parallel step
+(T = 32768, experts 32..63 local, with the stand-in expert); and the step at
+decode-like batch sizes (the first 64 and 256 tokens).
 """
 from __future__ import annotations
 
@@ -406,6 +407,42 @@ def bench_ep_share(tk, torch, np, synth, dev, steps):
             nbytes / (us - kern["standin"]) / 1e3 / PEAK_HBM_GBPS, 4)}}
 
 
+def bench_small_batch(tk, torch, logits, bias, x, y, opts, steps):
+    """The routing step at decode-like batch sizes: the first Ts tokens of the
+    same workload (Ts = 64 and 256, one map tile, so the map is one launch),
+    route + map + FP8 expand + combine, timed per step as a HIP graph (the
+    step is launch-bound; eager Python launches would dominate)."""
+    dev = logits.device
+    res = {}
+    for Ts in (64, 256):
+        R_s = Ts * K
+        idx = torch.empty((Ts, K), dtype=torch.int32, device=dev)
+        w = torch.empty((Ts, K), dtype=torch.float32, device=dev)
+        counts = torch.empty(E, dtype=torch.int32, device=dev)
+        offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        pos = torch.empty((Ts, K), dtype=torch.int32, device=dev)
+        row_src = torch.empty(R_s, dtype=torch.int32, device=dev)
+        ws = torch.empty(max(tk.tk_map_workspace_bytes(Ts, K, E), 16), dtype=torch.uint8,
+                         device=dev)
+        xq = torch.empty((R_s, H), dtype=torch.uint8, device=dev)
+        sc = torch.empty((R_s, NB), dtype=torch.float32, device=dev)
+        out = torch.empty((Ts, H), dtype=torch.bfloat16, device=dev)
+        lg, xs, ys = logits[:Ts], x[:Ts], y[:R_s]
+
+        def call():
+            tk.tk_route(lg, bias, K, opts, idx, w)
+            tk.tk_map(idx, E, 0, E, counts, offsets, pos, row_src, ws)
+            tk.tk_expand_quant(xs, pos, tk.TK_EXPAND_FP8_E4M3_1X128, R_s, xq, sc)
+            tk.tk_reduce(ys, pos, w, out)
+
+        us = _time_calls(torch, call, steps, [idx, w, pos, row_src, xq, sc, out])
+        res[f"T{Ts}"] = {"us_per_step": round(us, 2), "tokens_per_s": round(Ts / us * 1e6, 1)}
+    return {"small_batch": {
+        "workload": f"the first 64 / 256 tokens of the step's inputs (H={H}, E={E}, k={K}); "
+                    "route, map (one launch), FP8 expand, combine",
+        "timing": "HIP graph of the steps", "launches_per_step": 4, **res}}
+
+
 def bench_quant(tk, torch, x, steps):
     """Each codec granularity on the step's hidden states (8192 x 7168 bf16)."""
     out = {}
@@ -566,7 +603,8 @@ def main() -> int:
                  **bench_map_balance(tk, torch, logits, idx, args.steps),
                  **bench_quant(tk, torch, x, args.steps),
                  **bench_expand_bf16(tk, torch, x, pos, args.steps),
-                 **bench_ep_share(tk, torch, np, synth, dev, args.steps)}
+                 **bench_ep_share(tk, torch, np, synth, dev, args.steps),
+                 **bench_small_batch(tk, torch, logits, bias, x, y, opts, args.steps)}
 
     ms_per_step = total_ms / args.steps
     value = T / (ms_per_step * 1e-3)

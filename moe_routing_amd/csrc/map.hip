@@ -4,8 +4,9 @@
 // item moe/).
 //
 // Tokens are cut into tiles of 32*S <= 256 tokens (S sub-tiles of 32), one
-// token per thread.  Two launches at the usual sizes, no atomics on global
-// memory, so every output is a pure function of topk_idx:
+// token per thread.  Two launches at the usual sizes (one when all tokens fit
+// in one tile: map_single_kernel), no atomics on global memory, so every
+// output is a pure function of topk_idx:
 //   1. count  one workgroup per tile: LDS histogram of the tile's local
 //             routes -> cnt[tile][e] (tile-major: each tile writes whole
 //             lines of its own) in the workspace
@@ -293,6 +294,106 @@ __global__ __launch_bounds__(kThreads) void map_place_kernel(
     }
 }
 
+// All tokens in one tile (T <= the tile size): one workgroup does the whole
+// map in one launch.  Each expert's count is the popcount of its sub-tile
+// masks, so no count matrix and no second launch are needed; the offsets
+// scan and the positions are those of the place kernel.
+template <int KMAX>
+__global__ __launch_bounds__(kThreads) void map_single_kernel(
+    const int32_t* __restrict__ idx, int T, int k, int lo, int hi, int S, int align,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ pos,
+    int32_t* __restrict__ row_src)
+{
+    extern __shared__ uint32_t lds[];
+    __shared__ int32_t wave_sums[kThreads / tk::kWave];
+    const int nl = hi - lo;
+    uint32_t* mask = lds;                                          // [nl][S]
+    uint32_t* before_sub = lds + nl * S;                           // [nl][S]
+    int32_t* base = reinterpret_cast<int32_t*>(lds + 2 * nl * S);  // [nl]
+    const int t = threadIdx.x;
+    const bool mine = t < S * kSub && t < T;
+
+    int raw[KMAX];
+    if (mine) load_raw_ids<KMAX>(idx, t, k, raw);
+    for (int i = threadIdx.x; i < nl * S; i += kThreads) mask[i] = 0;
+    int e[KMAX];
+    if (mine) local_ids<KMAX>(raw, k, lo, hi, e);
+    __syncthreads();
+    if (mine) {
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+            if (e[j] >= 0) atomicOr(&mask[e[j] * S + t / kSub], 1u << (t % kSub));
+    }
+    __syncthreads();
+
+    // per expert (this thread owns [e0, e0 + ept), ept <= 4): sub-tile
+    // prefixes and the count; offsets = exclusive scan of the padded counts
+    constexpr int kMaxEpt = TK_MAX_EXPERTS / kThreads;
+    const int ept = (nl + kThreads - 1) / kThreads;
+    const int e0 = threadIdx.x * ept;
+    int32_t tot[kMaxEpt];
+    int32_t my_total = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxEpt; ++i) {
+        tot[i] = 0;
+        const int ex = e0 + i;
+        if (i >= ept || ex >= nl) continue;
+        uint32_t m[kMaxSub];
+#pragma unroll
+        for (int sb = 0; sb < kMaxSub; ++sb) m[sb] = mask[ex * S + (sb < S ? sb : S - 1)];
+        uint32_t r = 0;
+#pragma unroll
+        for (int sb = 0; sb < kMaxSub; ++sb) {
+            if (sb >= S) break;
+            before_sub[ex * S + sb] = r;
+            r += __popc(m[sb]);
+        }
+        tot[i] = static_cast<int32_t>(r);
+        my_total += (tot[i] + align - 1) / align * align;
+    }
+    int32_t grand = 0;
+    int32_t run = block_exclusive_scan(my_total, wave_sums, &grand);   // syncs the block
+#pragma unroll
+    for (int i = 0; i < kMaxEpt; ++i) {
+        const int ex = e0 + i;
+        if (i >= ept || ex >= nl) continue;
+        const int32_t padded = (tot[i] + align - 1) / align * align;
+        counts[ex] = tot[i];
+        offsets[ex] = run;
+        if (row_src != nullptr)   // padding rows have no source token
+            for (int32_t r = run + tot[i]; r < run + padded; ++r) row_src[r] = -1;
+        base[ex] = run;
+        run += padded;
+    }
+    if (threadIdx.x == 0) offsets[nl] = grand;
+    __syncthreads();
+
+    if (!mine) return;
+    const uint32_t below = (1u << (t % kSub)) - 1u;
+    const int sb = t / kSub;
+    int32_t bb[KMAX];
+    uint32_t bs[KMAX], mk[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        if (j >= k) break;
+        const int ee = e[j] >= 0 ? e[j] : 0;
+        const int w = ee * S + sb;
+        bb[j] = base[ee];
+        bs[j] = before_sub[w];
+        mk[j] = mask[w];
+    }
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        if (j >= k) break;
+        int32_t p = -1;
+        if (e[j] >= 0) {
+            p = bb[j] + static_cast<int32_t>(bs[j] + __popc(mk[j] & below));
+            if (row_src != nullptr) row_src[p] = t;
+        }
+        pos[static_cast<size_t>(t) * k + j] = p;
+    }
+}
+
 // Zero counts and offsets when no token is given.
 __global__ void map_empty_kernel(int nl, int32_t* __restrict__ counts, int32_t* __restrict__ offsets)
 {
@@ -357,6 +458,15 @@ TK_EXPORT tk_status tk_map_aligned(const int32_t* topk_idx, int32_t T, int32_t k
     int32_t* totals = cnt + static_cast<size_t>(g.n_tiles) * nl;
     const dim3 grid(g.n_tiles), block(kThreads);
     const bool small_k = k <= 8;
+    const size_t lds = (2 * static_cast<size_t>(nl) * g.S + nl) * sizeof(uint32_t);
+    if (g.n_tiles == 1) {
+        e = small_k
+            ? tk::launch(map_single_kernel<8>, grid, block, lds, stream, topk_idx, T, k,
+                         local_begin, local_end, g.S, align, counts, offsets, pos, row_src)
+            : tk::launch(map_single_kernel<TK_MAX_TOPK>, grid, block, lds, stream, topk_idx, T, k,
+                         local_begin, local_end, g.S, align, counts, offsets, pos, row_src);
+        return tk::launched(e, "tk_map (single tile)");
+    }
     e = small_k
         ? tk::launch(map_count_kernel<8>, grid, block, nl * sizeof(int32_t), stream, topk_idx, T, k,
                      local_begin, local_end, g.tile, cnt)
@@ -368,7 +478,6 @@ TK_EXPORT tk_status tk_map_aligned(const int32_t* topk_idx, int32_t T, int32_t k
                        totals);
         if (e != hipSuccess) return tk::launched(e, "tk_map (scan)");
     }
-    const size_t lds = (2 * static_cast<size_t>(nl) * g.S + nl) * sizeof(uint32_t);
     e = small_k
         ? tk::launch(map_place_kernel<8>, grid, block, lds, stream, topk_idx, T, k, local_begin,
                      local_end, g.S, g.n_tiles, g.fused ? 1 : 0, align, cnt, totals,

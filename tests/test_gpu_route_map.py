@@ -136,6 +136,9 @@ def test_map_v3_gate_full():
     (1, 8, 1, 0, 8), (31, 16, 2, 0, 16), (1000, 256, 8, 32, 64), (4097, 256, 8, 0, 256),
     (777, 64, 3, 0, 64), (300, 1024, 32, 0, 1024), (512, 1024, 9, 100, 900),
     (2049, 32, 4, 7, 8), (5000, 160, 6, 0, 160), (70000, 256, 8, 0, 256),
+    # one tile (the single-launch map): a full 256-token tile, a masked range,
+    # 1024 experts (160-token tiles) with k = 32, the tiny softmax shape
+    (256, 256, 8, 0, 256), (200, 64, 5, 10, 50), (160, 1024, 32, 0, 1024), (64, 16, 2, 0, 16),
 ])
 def test_map_random_routing(T, E, k, lo, hi):
     rng = np.random.default_rng(T + E)
@@ -143,17 +146,19 @@ def test_map_random_routing(T, E, k, lo, hi):
     _assert_map(idx, E, lo, hi)
 
 
-def test_map_repeats_and_out_of_range_ids():
+@pytest.mark.parametrize("T", [600, 100])   # three tiles; one tile
+def test_map_repeats_and_out_of_range_ids(T):
     rng = np.random.default_rng(7)
-    T, E, k = 600, 32, 6
+    E, k = 32, 6
     idx = rng.integers(-3, E + 3, (T, k)).astype(np.int32)   # repeats and invalid ids
     _assert_map(idx, E, 0, E)
     _assert_map(idx, E, 10, 20)
 
 
-def test_map_empty_experts_and_all_masked():
+@pytest.mark.parametrize("T", [500, 100])   # two tiles; one tile
+def test_map_empty_experts_and_all_masked(T):
     rng = np.random.default_rng(8)
-    idx = synth.random_routing(rng, 500, 16, 4) + 16          # all ids in [16, 32)
+    idx = synth.random_routing(rng, T, 16, 4) + 16            # all ids in [16, 32)
     (c, o, p, _), _ = _map_both(idx.astype(np.int32), 64, 0, 16)
     assert np.all(c == 0) and np.all(o == 0) and np.all(p == -1)
 
@@ -178,6 +183,7 @@ def test_map_deterministic():
     (1, 8, 1, 0, 8, 128), (300, 16, 2, 0, 16, 1), (1000, 256, 8, 32, 64, 128),
     (4097, 256, 8, 0, 256, 128), (777, 64, 3, 0, 64, 7), (2049, 32, 4, 7, 8, 1000),
     (70000, 256, 8, 0, 256, 64), (300, 1024, 32, 0, 1024, 16),
+    (200, 256, 8, 0, 256, 128), (100, 1024, 32, 0, 1024, 16), (64, 64, 4, 8, 40, 3),
 ])
 def test_map_aligned_random_routing(T, E, k, lo, hi, align):
     rng = np.random.default_rng(T + E + align)
