@@ -48,7 +48,7 @@ struct Tiling {
 __host__ inline Tiling tiling(int T, int n_local)
 {
     Tiling g{};
-    int s_max = (kLdsWords - n_local) / (2 * n_local);  // mask + before words per tile
+    int s_max = (kLdsWords - 3 * n_local) / (2 * n_local);  // mask + before words per tile
     s_max = s_max < 1 ? 1 : (s_max > kMaxSub ? kMaxSub : s_max);
     const int s = (T + kSub - 1) / kSub;                 // no more sub-tiles than tokens need
     g.S = s < 1 ? 1 : (s > s_max ? s_max : s);
@@ -163,6 +163,21 @@ __device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* wave
     return before + inc - v;
 }
 
+// row_src = -1 on the padding rows at the end of each expert's segment (they
+// have no source token).  The n_tiles workgroups share the experts (tile,
+// tile + n_tiles, ...); a workgroup's threads write one expert's run of
+// padding rows together, so the stores are coalesced and no workgroup walks
+// every segment.
+__device__ __forceinline__ void write_padding(int32_t* __restrict__ row_src,
+                                              const int32_t* pad_off, const int32_t* pad_cnt,
+                                              int nl, int tile, int n_tiles)
+{
+    for (int ex = tile; ex < nl; ex += n_tiles) {
+        const int32_t o = pad_off[ex], n = pad_cnt[ex];
+        for (int i = threadIdx.x; i < n; i += kThreads) row_src[o + i] = -1;
+    }
+}
+
 template <int KMAX>
 __global__ __launch_bounds__(kThreads) void map_place_kernel(
     const int32_t* __restrict__ idx, int T, int k, int lo, int hi, int S, int n_tiles, int fused, int align, const int32_t* __restrict__ cnt, const int32_t* __restrict__ totals,
@@ -175,6 +190,8 @@ __global__ __launch_bounds__(kThreads) void map_place_kernel(
     uint32_t* mask = lds;                                          // [nl][S]
     uint32_t* before_sub = lds + nl * S;                           // [nl][S]
     int32_t* base = reinterpret_cast<int32_t*>(lds + 2 * nl * S);  // [nl]
+    int32_t* pad_off = base + nl;                                  // [nl] first padding row
+    int32_t* pad_cnt = pad_off + nl;                               // [nl] padding rows
     const int tile = blockIdx.x;
     const int tile_tokens = S * kSub;
     const int tl = threadIdx.x;
@@ -240,14 +257,15 @@ __global__ __launch_bounds__(kThreads) void map_place_kernel(
         if (tile == 0) {
             counts[ex] = tot;
             offsets[ex] = run;
-            if (row_src != nullptr)   // padding rows have no source token
-                for (int32_t r = run + tot; r < run + padded; ++r) row_src[r] = -1;
         }
+        pad_off[ex] = run + tot;
+        pad_cnt[ex] = padded - tot;
         base[ex] += run;
         run += padded;
     }
     if (tile == 0 && threadIdx.x == 0) offsets[nl] = grand;
     __syncthreads();
+    if (row_src != nullptr && align > 1) write_padding(row_src, pad_off, pad_cnt, nl, tile, n_tiles);
 
     // 3. tokens of each expert in the earlier sub-tiles of this tile (the
     //    expert's S mask words are read into registers before any prefix is
@@ -310,6 +328,8 @@ __global__ __launch_bounds__(kThreads) void map_single_kernel(
     uint32_t* mask = lds;                                          // [nl][S]
     uint32_t* before_sub = lds + nl * S;                           // [nl][S]
     int32_t* base = reinterpret_cast<int32_t*>(lds + 2 * nl * S);  // [nl]
+    int32_t* pad_off = base + nl;                                  // [nl] first padding row
+    int32_t* pad_cnt = pad_off + nl;                               // [nl] padding rows
     const int t = threadIdx.x;
     const bool mine = t < S * kSub && t < T;
 
@@ -360,13 +380,14 @@ __global__ __launch_bounds__(kThreads) void map_single_kernel(
         const int32_t padded = (tot[i] + align - 1) / align * align;
         counts[ex] = tot[i];
         offsets[ex] = run;
-        if (row_src != nullptr)   // padding rows have no source token
-            for (int32_t r = run + tot[i]; r < run + padded; ++r) row_src[r] = -1;
+        pad_off[ex] = run + tot[i];
+        pad_cnt[ex] = padded - tot[i];
         base[ex] = run;
         run += padded;
     }
     if (threadIdx.x == 0) offsets[nl] = grand;
     __syncthreads();
+    if (row_src != nullptr && align > 1) write_padding(row_src, pad_off, pad_cnt, nl, 0, 1);
 
     if (!mine) return;
     const uint32_t below = (1u << (t % kSub)) - 1u;
@@ -458,7 +479,7 @@ TK_EXPORT tk_status tk_map_aligned(const int32_t* topk_idx, int32_t T, int32_t k
     int32_t* totals = cnt + static_cast<size_t>(g.n_tiles) * nl;
     const dim3 grid(g.n_tiles), block(kThreads);
     const bool small_k = k <= 8;
-    const size_t lds = (2 * static_cast<size_t>(nl) * g.S + nl) * sizeof(uint32_t);
+    const size_t lds = (2 * static_cast<size_t>(nl) * g.S + 3 * nl) * sizeof(uint32_t);
     if (g.n_tiles == 1) {
         e = small_k
             ? tk::launch(map_single_kernel<8>, grid, block, lds, stream, topk_idx, T, k,

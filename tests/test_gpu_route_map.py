@@ -137,8 +137,8 @@ def test_map_v3_gate_full():
     (777, 64, 3, 0, 64), (300, 1024, 32, 0, 1024), (512, 1024, 9, 100, 900),
     (2049, 32, 4, 7, 8), (5000, 160, 6, 0, 160), (70000, 256, 8, 0, 256),
     # one tile (the single-launch map): a full 256-token tile, a masked range,
-    # 1024 experts (160-token tiles) with k = 32, the tiny softmax shape
-    (256, 256, 8, 0, 256), (200, 64, 5, 10, 50), (160, 1024, 32, 0, 1024), (64, 16, 2, 0, 16),
+    # 1024 experts (128-token tiles) with k = 32, the tiny softmax shape
+    (256, 256, 8, 0, 256), (200, 64, 5, 10, 50), (128, 1024, 32, 0, 1024), (64, 16, 2, 0, 16),
 ])
 def test_map_random_routing(T, E, k, lo, hi):
     rng = np.random.default_rng(T + E)
