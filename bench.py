@@ -8,7 +8,8 @@ One step = the whole path over one batch of the DeepSeek-V3-shaped workload
                    groups, top-8 experts, weights normalised * 2.5
   tk_map           counts, offsets, stable positions (no mask: all local)
   tk_expand_quant  1x128 FP8 E4M3 expand into 65536 expert-contiguous rows
-  tk_reduce        bf16 combine of 65536 expert-output rows, fp32 accumulate
+  tk_reduce_dense  bf16 combine of 65536 expert-output rows, fp32 accumulate
+                   (tk_reduce's dense form: every slot has a row here)
 
 Inputs are synthetic (seeded normal logits, U(-0.1,0.1) bias, bf16 N(0,1)
 hidden states with 1 % outlier rows x50, bf16 N(0,1) expert outputs) and
@@ -530,7 +531,7 @@ def main() -> int:
         tk.tk_expand_quant(x, pos, tk.TK_EXPAND_FP8_E4M3_1X128, R, xq, sc)
         if ev is not None:
             ev[3].record()
-        tk.tk_reduce(y, pos, w, out)
+        tk.tk_reduce_dense(y, pos, w, out)
         if ev is not None:
             ev[4].record()
 
@@ -649,7 +650,7 @@ def main() -> int:
         "kernel_gbps": {s: round(BYTES[s] / (kern_us[s] * 1e-6) / 1e9, 1) for s in steps},
         "wall_s_timed": round(wall, 4),
         "kernel_breakdown": "second pass of the same steps with an event between calls",
-        "roofline": {"kernel": "reduce_kernel<8>", "bound": "hbm", "achieved": round(achieved, 1),
+        "roofline": {"kernel": "reduce_staged_kernel<8>", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic,

@@ -11,6 +11,8 @@
  *   tk_expand_quant  expand into expert-contiguous rows,    (x -> rows [+ FP8
  *                    optionally fused 1x128 FP8 E4M3 quant    scales])
  *   tk_reduce        weighted combine back to tokens        (rows, w -> out)
+ *   tk_reduce_dense  the same, faster when (nearly) every
+ *                    slot has a row
  *
  * quantisation at other granularities (power-of-two scales, 128x128 tiles,
  * per channel, FP4),
@@ -251,6 +253,20 @@ tk_status tk_expand_quant(const void* x_bf16, int32_t T, int32_t H, int32_t k,
  */
 tk_status tk_reduce(const void* y_bf16, int64_t rows, const int32_t* pos, const float* topk_w,
                     int32_t T, int32_t k, int32_t H, void* out_bf16, hipStream_t stream);
+
+/*
+ * tk_reduce_dense -- tk_reduce for dense routings: the same arguments,
+ * checks, errors and bit-identical results.  It combines a few consecutive
+ * tokens per workgroup into LDS and writes their rows as one burst, which
+ * pays off when (nearly) every slot has a row -- no local-expert mask, as in
+ * a single-GPU layer -- and loses to tk_reduce when most slots are masked
+ * (one GPU's share of an expert-parallel layer).  It takes tk_reduce's kernel
+ * itself for small T (fewer tokens than one burst per compute unit), runtime
+ * k (k not in {1, 2, 4, 6, 8}) and rows too long for its LDS budget.
+ */
+tk_status tk_reduce_dense(const void* y_bf16, int64_t rows, const int32_t* pos,
+                          const float* topk_w, int32_t T, int32_t k, int32_t H, void* out_bf16,
+                          hipStream_t stream);
 
 /*
  * tk_swiglu_quant_t -- the transposing form of the same fusion (SwiGLU + FP8

@@ -11,6 +11,7 @@ step of the path runs in the library's HIP kernels; there is no fallback.
     tk_map_aligned(topk_idx, E, local_begin, local_end, align) -> (counts, offsets, pos, row_src)
     tk_expand_quant(x, pos, mode, rows_capacity) -> (out, scales)
     tk_reduce(y, pos, topk_w)                  -> out
+    tk_reduce_dense(y, pos, topk_w)            -> out (the same, dense routings)
     tk_expert_standin(xq, scales, n_rows, mult) -> y
     tk_swiglu_quant(h, I, n_rows, row_src, pos, topk_w) -> (out, scales)
     tk_swiglu_quant_t(h, row_src, pos, topk_w) -> (out, scales, out_t, scales_t)
@@ -93,6 +94,8 @@ def library() -> ctypes.CDLL:
         L.tk_expand_quant.restype = i32
         L.tk_reduce.argtypes = [vp, i64, vp, vp, i32, i32, i32, vp, vp]
         L.tk_reduce.restype = i32
+        L.tk_reduce_dense.argtypes = [vp, i64, vp, vp, i32, i32, i32, vp, vp]
+        L.tk_reduce_dense.restype = i32
         L.tk_expert_standin.argtypes = [vp, vp, vp, i64, i32, f32, vp, vp]
         L.tk_expert_standin.restype = i32
         L.tk_swiglu_quant.argtypes = [vp, i64, vp, i32, vp, vp, vp, i32, i32, vp, vp, vp]
@@ -237,6 +240,17 @@ def tk_expand_quant(x: torch.Tensor, pos: torch.Tensor, mode: int, rows_capacity
 
 def tk_reduce(y: torch.Tensor, pos: torch.Tensor, topk_w: torch.Tensor,
               out: torch.Tensor | None = None):
+    return _reduce("tk_reduce", y, pos, topk_w, out)
+
+
+def tk_reduce_dense(y: torch.Tensor, pos: torch.Tensor, topk_w: torch.Tensor,
+                    out: torch.Tensor | None = None):
+    """tk_reduce for routings where (nearly) every slot has a row: the same
+    results, one burst of output rows per few tokens."""
+    return _reduce("tk_reduce_dense", y, pos, topk_w, out)
+
+
+def _reduce(fn: str, y, pos, topk_w, out):
     _dev(y, "y", torch.bfloat16, 2)
     dev = y.device
     _dev(pos, "pos", torch.int32, 2, device=dev)
@@ -248,8 +262,8 @@ def tk_reduce(y: torch.Tensor, pos: torch.Tensor, topk_w: torch.Tensor,
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     _dev(out, "out", torch.bfloat16, 2, T * H, dev)
-    _check("tk_reduce", library().tk_reduce(_ptr(y), R, _ptr(pos), _ptr(topk_w), T, k, H,
-                                            _ptr(out), _stream(y)))
+    _check(fn, getattr(library(), fn)(_ptr(y), R, _ptr(pos), _ptr(topk_w), T, k, H, _ptr(out),
+                                      _stream(y)))
     return out
 
 

@@ -30,7 +30,7 @@ def lib():
     L = ctypes.CDLL(LIB)
     L.tk_last_error.restype = ctypes.c_char_p
     for name in ("tk_route", "tk_map", "tk_map_aligned", "tk_expand_quant", "tk_reduce",
-                 "tk_expert_standin", "tk_swiglu_quant", "tk_swiglu_quant_t",
+                 "tk_reduce_dense", "tk_expert_standin", "tk_swiglu_quant", "tk_swiglu_quant_t",
                                   "tk_silu_bf16", "tk_balance_loss",
                  "tk_quant"):
         getattr(L, name).restype = ctypes.c_int32
@@ -43,7 +43,7 @@ def lib():
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["tk_last_error", "tk_route", "tk_map_workspace_bytes", "tk_map",
                                   "tk_map_aligned", "tk_expand_quant", "tk_reduce",
-                                  "tk_expert_standin", "tk_swiglu_quant", "tk_swiglu_quant_t",
+                                  "tk_reduce_dense", "tk_expert_standin", "tk_swiglu_quant", "tk_swiglu_quant_t",
                                   "tk_silu_bf16",
                                   "tk_balance_workspace_bytes", "tk_balance_loss",
                                   "tk_quant_workspace_bytes", "tk_quant"])
@@ -152,9 +152,10 @@ def test_expand_rejects_bad_arguments(lib):
     assert _expand(lib, 0, 256, 2, 1, 8, x=None, out=None, pos=None) == 0
 
 
-def test_reduce_and_standin_reject_bad_arguments(lib):
+@pytest.mark.parametrize("fn", ["tk_reduce", "tk_reduce_dense"])
+def test_reduce_and_standin_reject_bad_arguments(lib, fn):
     I = ctypes.c_int32
-    r = lambda T, k, H, rows=8, y=FAKE, out=FAKE: lib.tk_reduce(
+    r = lambda T, k, H, rows=8, y=FAKE, out=FAKE: getattr(lib, fn)(
         y, ctypes.c_int64(rows), FAKE, FAKE, I(T), I(k), I(H), out, None)
     assert r(-1, 2, 256) == ARG
     assert r(4, 0, 256) == ARG

@@ -172,8 +172,8 @@ def test_standin_matches_oracle():
 
 
 # ------------------------------------------------------------------ reduce --
-def _check_reduce(y_bits, pos, w, sample=None):
-    out = tk.tk_reduce(to_dev(y_bits, bf16=True), to_dev(pos), to_dev(w))
+def _check_reduce(y_bits, pos, w, sample=None, fn="tk_reduce"):
+    out = getattr(tk, fn)(to_dev(y_bits, bf16=True), to_dev(pos), to_dev(w))
     torch.cuda.synchronize()
     g = to_host(out)
     if sample is None:
@@ -212,6 +212,36 @@ def test_reduce_few_tokens(T, k):
     _check_reduce(y, pos, w)
 
 
+# tk_reduce_dense: at T >= (compute units) x (tokens per workgroup) it takes its
+# staged form (a workgroup combines a few consecutive tokens into LDS and
+# writes their rows as one burst); tk_reduce and slices of fewer than 2048
+# tokens take the one-wave-per-unit kernel.  Per token the arithmetic is the
+# same, so all must agree bit for bit; both stay within the combine tolerance
+# of the oracle.  Cases: every compiled k, a ragged last burst, a 520-column
+# row (a partly filled 512-column unit), masked slots and rows beyond y.
+@pytest.mark.parametrize("T,k,H", [(2048, 8, 7168), (4100, 8, 1024), (5000, 6, 2048),
+                                   (3000, 4, 4096), (2600, 2, 520), (2049, 1, 1024)])
+def test_reduce_dense_equals_reduce(T, k, H):
+    rng = np.random.default_rng(T + 10 * k + H)
+    R = T * k
+    pos = rng.permutation(R).astype(np.int32).reshape(T, k)
+    pos[rng.random((T, k)) < 0.1] = -1                      # masked slots
+    rows = R - R // 50                                      # the last rows are beyond y
+    y = synth.normal_bf16(rng, (rows, H))
+    w = rng.random((T, k)).astype(np.float32)
+    yd, pd, wd = to_dev(y, bf16=True), to_dev(pos), to_dev(w)
+    dense = to_host(tk.tk_reduce_dense(yd, pd, wd))
+    plain = to_host(tk.tk_reduce(yd, pd, wd))
+    sliced = np.concatenate([to_host(tk.tk_reduce_dense(yd, pd[a:a + 1000], wd[a:a + 1000]))
+                             for a in range(0, T, 1000)])
+    assert np.array_equal(dense, plain)
+    assert np.array_equal(dense, sliced)
+    sample = np.random.default_rng(T).choice(T, 300, replace=False)
+    ref = oracle.reduce(y, pos[sample], w[sample])
+    rep = combine_report(dense[sample], ref)
+    assert rep["ok"] and rep["bit_exact_frac"] > 0.98, rep
+
+
 def test_reduce_masked_and_empty_tokens():
     T, E, k, H = 400, 64, 8, 1024
     idx, pos, R = _routing(T, E, k, 31, lo=32, hi=40)
@@ -232,11 +262,12 @@ def test_reduce_exact_gather():
     assert np.array_equal(to_host(out), y[perm[:, 0]])
 
 
-def test_reduce_v3_full_sampled():
+@pytest.mark.parametrize("fn", ["tk_reduce", "tk_reduce_dense"])   # the bench's step takes the second
+def test_reduce_v3_full_sampled(fn):
     cfg = synth.v3_gate(0)
     idx, w = oracle.route(cfg["logits"], cfg["bias"], cfg["k"], **cfg["route"])
     _, offsets, pos, _ = oracle.map_routes(idx, 256)
     y = synth.v3_expert_out(0)
     sample = np.random.default_rng(35).choice(8192, 256, replace=False)
     sample = np.concatenate([sample, [0, 8191]])
-    _check_reduce(y, pos, w.astype(np.float32), sample)
+    _check_reduce(y, pos, w.astype(np.float32), sample, fn)

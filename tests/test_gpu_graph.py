@@ -23,7 +23,8 @@ T, E, K, H = 4096, 256, 8, 2048
 class Step:
     """Inputs and preallocated outputs of one routing step."""
 
-    def __init__(self, seed: int, dev):
+    def __init__(self, seed: int, dev, reduce: str = "tk_reduce"):
+        self.reduce = getattr(tk, reduce)
         g = torch.Generator().manual_seed(seed)
         self.logits = torch.randn((T, E), generator=g).to(dev)
         self.bias = (torch.rand(E, generator=g) * 0.2 - 0.1).to(dev)
@@ -46,7 +47,7 @@ class Step:
         tk.tk_route(self.logits, self.bias, K, self.opts, self.idx, self.w)
         tk.tk_map(self.idx, E, 0, E, self.counts, self.offsets, self.pos, self.row_src, self.ws)
         tk.tk_expand_quant(self.x, self.pos, tk.TK_EXPAND_FP8_E4M3_1X128, T * K, self.xq, self.sc)
-        tk.tk_reduce(self.y, self.pos, self.w, self.out)
+        self.reduce(self.y, self.pos, self.w, self.out)
 
     def outputs(self):
         return [self.idx, self.w, self.counts, self.offsets, self.pos, self.row_src, self.xq,
@@ -60,10 +61,12 @@ def _same(a, b):
     return all(torch.equal(u, v) for u, v in zip(a, b))
 
 
-def test_step_replays_from_a_graph():
+# both combines: at T=4096, H=2048 tk_reduce_dense takes its staged form
+@pytest.mark.parametrize("reduce", ["tk_reduce", "tk_reduce_dense"])
+def test_step_replays_from_a_graph(reduce):
     dev = torch.device("cuda:0")
-    s = Step(1, dev)
-    other = Step(2, dev)
+    s = Step(1, dev, reduce)
+    other = Step(2, dev, reduce)
     s.run()
     torch.cuda.synchronize()
     ref = s.snapshot()
@@ -90,9 +93,10 @@ def test_step_replays_from_a_graph():
         assert _same(s.outputs(), ref), f"replay {replay} differs from the eager step"
 
 
-def test_two_steps_on_concurrent_streams():
+@pytest.mark.parametrize("reduce", ["tk_reduce", "tk_reduce_dense"])
+def test_two_steps_on_concurrent_streams(reduce):
     dev = torch.device("cuda:0")
-    a, b = Step(3, dev), Step(4, dev)
+    a, b = Step(3, dev, reduce), Step(4, dev, reduce)
     a.run()
     b.run()
     torch.cuda.synchronize()
