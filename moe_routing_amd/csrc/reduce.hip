@@ -89,26 +89,28 @@ __global__ __launch_bounds__(tk::kWave * kWavesPerGroup) void reduce_kernel(
     }
 }
 
-constexpr int kPhThreads = 1024;                       // 16 waves per workgroup (dense form)
-constexpr int kPhWaves = kPhThreads / tk::kWave;
-constexpr int kPhLdsBytes = 112 * 1024;                // staged output rows per workgroup
+constexpr int kStThreads = 1024;                       // 16 waves per workgroup (dense form)
+constexpr int kStWaves = kStThreads / tk::kWave;
+constexpr int kStLdsBytes = 112 * 1024;                // staged output rows per workgroup
 constexpr int kMaxDevices = 64;
 
 template <int K>
-__global__ __launch_bounds__(kPhThreads) void reduce_staged_kernel(
+__global__ __launch_bounds__(kStThreads) void reduce_staged_kernel(
     const uint16_t* __restrict__ y, int64_t rows_in, const int32_t* __restrict__ pos,
     const float* __restrict__ w, int T, int H, int chunks, int tpw, uint16_t* __restrict__ out)
 {
     extern __shared__ __align__(16) uint16_t staged[];   // [tpw][H] bf16
     const int lane = threadIdx.x & (tk::kWave - 1);
     const int wave = tk::uniform(threadIdx.x / tk::kWave);
-    const int per_phase = gridDim.x * tpw;
-    for (int base = 0; base < T; base += per_phase) {     // the same count in every thread
-        const int t0 = base + blockIdx.x * tpw;
-        int nt = T - t0;
-        nt = nt < 0 ? 0 : (nt > tpw ? tpw : nt);
+    // one pass when the grid covers T (as launched); any grid is correct
+    const int64_t per_pass = static_cast<int64_t>(gridDim.x) * tpw;
+    for (int64_t base = 0; base < T; base += per_pass) {   // the same count in every thread
+        const int64_t t_first = base + static_cast<int64_t>(blockIdx.x) * tpw;
+        const int64_t left = T - t_first;
+        const int nt = left <= 0 ? 0 : (left > tpw ? tpw : static_cast<int>(left));
+        const int t0 = nt > 0 ? static_cast<int>(t_first) : 0;
         const int units = nt * chunks;
-        for (int u = wave; u < units; u += kPhWaves) {
+        for (int u = wave; u < units; u += kStWaves) {
             const int tl = u / chunks;
             const int t = t0 + tl;
             const int col = (u - tl * chunks) * kChunk + lane * 8;
@@ -155,8 +157,8 @@ __global__ __launch_bounds__(kPhThreads) void reduce_staged_kernel(
         __syncthreads();
         // rows t0 .. t0 + nt - 1 are contiguous in out: one burst of 16-byte stores
         const int n16 = nt * (H / 8);
-        uint16_t* dst = out + static_cast<size_t>(nt > 0 ? t0 : 0) * H;
-        for (int i = threadIdx.x; i < n16; i += kPhThreads)
+        uint16_t* dst = out + static_cast<size_t>(t0) * H;
+        for (int i = threadIdx.x; i < n16; i += kStThreads)
             tk::store_stream(dst + static_cast<size_t>(i) * 8,
                              *reinterpret_cast<const tk::u32x4*>(staged + static_cast<size_t>(i) * 8));
         __syncthreads();   // the staged rows are read out before the next tokens
@@ -168,7 +170,7 @@ __global__ __launch_bounds__(kPhThreads) void reduce_staged_kernel(
 int staged_tokens(int H, int chunks)
 {
     for (int tpw : {8, 4, 2})
-        if (static_cast<int64_t>(tpw) * H * 2 <= kPhLdsBytes && (tpw * chunks) % kPhWaves == 0)
+        if (static_cast<int64_t>(tpw) * H * 2 <= kStLdsBytes && (tpw * chunks) % kStWaves == 0)
             return tpw;
     return 0;
 }
@@ -184,8 +186,8 @@ int device_cus(int dev)
     return n > 0 ? n : 0;
 }
 
-// Lets reduce_staged_kernel<K> use kPhLdsBytes of LDS on `dev` (once per
-// device); false if the device refuses, and the caller then takes the
+// Lets reduce_staged_kernel<K> use kStLdsBytes of LDS on `dev` (once per
+// device); false if the device refuses, and the call then takes the
 // one-wave-per-unit kernel.
 template <int K>
 bool staged_lds_ready(int dev)
@@ -194,7 +196,7 @@ bool staged_lds_ready(int dev)
     if (dev < 0 || dev >= kMaxDevices) return false;
     if (ready[dev].load(std::memory_order_acquire)) return true;
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(reduce_staged_kernel<K>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kPhLdsBytes) != hipSuccess) {
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kStLdsBytes) != hipSuccess) {
         (void)hipGetLastError();   // not sticky: the fallback launch must not see it
         return false;
     }
@@ -213,15 +215,11 @@ bool launch_staged(const uint16_t* y, int64_t rows, const int32_t* pos, const fl
     const int cus = device_cus(dev);
     if (cus == 0 || static_cast<int64_t>(T) < static_cast<int64_t>(cus) * tpw) return false;
     if (!staged_lds_ready<K>(dev)) return false;
-    *e = tk::launch(reduce_staged_kernel<K>, dim3(static_cast<unsigned>((T + tpw - 1) / tpw)),
-                    dim3(kPhThreads),
+    const int64_t groups = (static_cast<int64_t>(T) + tpw - 1) / tpw;
+    *e = tk::launch(reduce_staged_kernel<K>, dim3(static_cast<unsigned>(groups)), dim3(kStThreads),
                     static_cast<size_t>(tpw) * H * 2, stream, y, rows, pos, w, T, H, chunks, tpw, out);
     return true;
 }
-
-}  // namespace
-
-namespace {
 
 // Both entry points: argument checks, then the staged form (dense, when it
 // applies) or the one-wave-per-unit kernel.
