@@ -220,7 +220,9 @@ def test_reduce_few_tokens(T, k):
 # of the oracle.  Cases: every compiled k, a ragged last burst, a 520-column
 # row (a partly filled 512-column unit), masked slots and rows beyond y.
 @pytest.mark.parametrize("T,k,H", [(2048, 8, 7168), (4100, 8, 1024), (5000, 6, 2048),
-                                   (3000, 4, 4096), (2600, 2, 520), (2049, 1, 1024)])
+                                   (3000, 4, 4096), (2600, 2, 520), (2049, 1, 1024),
+                                   (2111, 6, 7168), (3333, 4, 7168), (2047, 8, 7168),
+                                   (2500, 8, 4096)])
 def test_reduce_dense_equals_reduce(T, k, H):
     rng = np.random.default_rng(T + 10 * k + H)
     R = T * k
@@ -239,6 +241,23 @@ def test_reduce_dense_equals_reduce(T, k, H):
     sample = np.random.default_rng(T).choice(T, 300, replace=False)
     ref = oracle.reduce(y, pos[sample], w[sample])
     rep = combine_report(dense[sample], ref)
+    assert rep["ok"] and rep["bit_exact_frac"] > 0.98, rep
+
+
+def test_reduce_dense_with_rows_cut_short():
+    # a short y (rows < T*k): the slots pointing past its end are skipped by
+    # both forms, as if masked -- a fifth of the rows are missing here
+    T, k, H = 4096, 8, 2048
+    rng = np.random.default_rng(77)
+    pos = rng.permutation(T * k).astype(np.int32).reshape(T, k)
+    rows = T * k * 4 // 5
+    y = synth.normal_bf16(rng, (rows, H))
+    w = rng.random((T, k)).astype(np.float32)
+    yd, pd, wd = to_dev(y, bf16=True), to_dev(pos), to_dev(w)
+    dense = to_host(tk.tk_reduce_dense(yd, pd, wd))
+    assert np.array_equal(dense, to_host(tk.tk_reduce(yd, pd, wd)))
+    sample = np.random.default_rng(78).choice(T, 200, replace=False)
+    rep = combine_report(dense[sample], oracle.reduce(y, pos[sample], w[sample]))
     assert rep["ok"] and rep["bit_exact_frac"] > 0.98, rep
 
 
