@@ -28,7 +28,8 @@ enter value: SwiGLU + 1x128 FP8 quantisation of the 65536 expanded rows at
 the DeepSeek-V3 expert width I = 2048 (plain and transposing), weighted by the
 routing weights through the step's map; the padded map; the balance loss;
 the other quantisation granularities of the hidden states; the expand without
-quantisation (bf16 rows); one GPU's share of an expert-parallel step
+quantisation (bf16 rows); both combines (tk_reduce_dense, the step's, and
+tk_reduce) on the step's data; one GPU's share of an expert-parallel step
 (T = 32768, experts 32..63 local, with the stand-in expert); and the step at
 decode-like batch sizes (the first 64 and 256 tokens).
 """
@@ -326,6 +327,22 @@ def bench_expand_bf16(tk, torch, x, pos, steps):
                                          "algorithmic_bytes": nbytes}}}
 
 
+def bench_combines(tk, torch, y, pos, w, steps):
+    """Both combines on the step's data, each as a HIP graph of the calls:
+    tk_reduce_dense (the step's) and tk_reduce (one wave per unit, the form
+    for routings where most slots are masked)."""
+    res = {}
+    for name in ("tk_reduce_dense", "tk_reduce"):
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+        fn = getattr(tk, name)
+        us = _time_calls(torch, lambda: fn(y, pos, w, out), min(steps, 20), (out,))
+        nb = BYTES["reduce"]
+        res[name] = {"us_per_call": round(us, 2), "hbm_gbps": round(nb / us / 1e3, 1),
+                     "frac": round(nb / us / 1e3 / PEAK_HBM_GBPS, 4)}
+    return {"combines": {"workload": f"the step's combine: y bf16 ({R}, {H}), k={K}, T={T}",
+                         "timing": "HIP graph of the calls", **res}}
+
+
 def bench_ep_share(tk, torch, np, synth, dev, steps):
     """The one-GPU share of an expert-parallel step: DeepSeek-V3 routing over
     T = 32768 tokens with experts 32..63 local (a log-Zipf popularity offset on
@@ -604,6 +621,7 @@ def main() -> int:
                  **bench_map_balance(tk, torch, logits, idx, args.steps),
                  **bench_quant(tk, torch, x, args.steps),
                  **bench_expand_bf16(tk, torch, x, pos, args.steps),
+                 **bench_combines(tk, torch, y, pos, w, args.steps),
                  **bench_ep_share(tk, torch, np, synth, dev, args.steps),
                  **bench_small_batch(tk, torch, logits, bias, x, y, opts, args.steps)}
 
