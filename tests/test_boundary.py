@@ -305,3 +305,14 @@ def test_calibration_library_exports_only_the_stream_copy():
     assert f(FAKE, FAKE, 24, None) == -1                     # not a multiple of 16
     assert f(MIS, FAKE, 32, None) == -1                      # misaligned source
     assert f(None, FAKE, 32, None) == -1
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # one GPU's path: --gpus N > 1 ends with a message and status 2, before
+    # anything touches a device
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in (r.stdout + r.stderr)
