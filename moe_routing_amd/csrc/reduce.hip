@@ -16,15 +16,17 @@
 // then one round-to-nearest-even conversion to bf16.
 //
 // tk_reduce_dense, the same combine for dense routings (every slot, or
-// nearly, has a row): one 1024-thread workgroup per `tpw` consecutive tokens
-// (8 at H = 7168) combines their rows into LDS -- the same units and
-// arithmetic as above, so the results are bit-identical -- and then writes
-// the tpw output rows as one contiguous burst.  With the writes grouped into
-// bursts the HBM bus turns between reads and writes less often: 174-177 ->
-// 171-172 us at T=8192, H=7168, k=8, while the same schedule with each unit
-// stored directly takes 201 us.  When most slots are masked (one GPU's
+// nearly, has a row): one 1024-thread workgroup takes up to 16 consecutive
+// tokens; each of its 16 waves combines up to 14 of their units -- the same
+// units and arithmetic as above, so the results are bit-identical -- keeps
+// the outputs in registers, and stores them only after a workgroup barrier,
+// so the workgroup's output rows (224 KiB at H = 7168) leave as one burst
+// after all of its reads.  With the writes grouped into bursts the HBM bus
+// turns between reads and writes less often: 174-177 -> 169-170 us at
+// T=8192, H=7168, k=8, while the same schedule with each unit stored as soon
+// as it is combined takes 201 us.  When most slots are masked (one GPU's
 // expert-parallel share: two thirds of the tokens have no local route) the
-// big LDS-bound workgroups lose to the many short waves of tk_reduce (171 vs
+// big workgroups lose to the many short waves of tk_reduce (170-190 vs
 // 122-136 us), and the call cannot see the routing, so the caller chooses.
 #include "tk_internal.h"
 
@@ -91,7 +93,8 @@ __global__ __launch_bounds__(tk::kWave * kWavesPerGroup) void reduce_kernel(
 
 constexpr int kStThreads = 1024;                       // 16 waves per workgroup (dense form)
 constexpr int kStWaves = kStThreads / tk::kWave;
-constexpr int kStLdsBytes = 112 * 1024;                // staged output rows per workgroup
+constexpr int kStUnits = 14;                           // units per wave at most
+constexpr int kStMaxTokens = 16;                       // tokens per workgroup at most
 constexpr int kMaxDevices = 64;
 
 template <int K>
@@ -99,80 +102,77 @@ __global__ __launch_bounds__(kStThreads) void reduce_staged_kernel(
     const uint16_t* __restrict__ y, int64_t rows_in, const int32_t* __restrict__ pos,
     const float* __restrict__ w, int T, int H, int chunks, int tpw, uint16_t* __restrict__ out)
 {
-    extern __shared__ __align__(16) uint16_t staged[];   // [tpw][H] bf16
     const int lane = threadIdx.x & (tk::kWave - 1);
     const int wave = tk::uniform(threadIdx.x / tk::kWave);
-    // one pass when the grid covers T (as launched); any grid is correct
-    const int64_t per_pass = static_cast<int64_t>(gridDim.x) * tpw;
-    for (int64_t base = 0; base < T; base += per_pass) {   // the same count in every thread
-        const int64_t t_first = base + static_cast<int64_t>(blockIdx.x) * tpw;
-        const int64_t left = T - t_first;
-        const int nt = left <= 0 ? 0 : (left > tpw ? tpw : static_cast<int>(left));
-        const int t0 = nt > 0 ? static_cast<int>(t_first) : 0;
-        const int units = nt * chunks;
-        for (int u = wave; u < units; u += kStWaves) {
-            const int tl = u / chunks;
-            const int t = t0 + tl;
-            const int col = (u - tl * chunks) * kChunk + lane * 8;
-            const int32_t* p = pos + static_cast<size_t>(t) * K;
-            const float* wt = w + static_cast<size_t>(t) * K;
-            int32_t r32[K];
-            float wj[K];
+    const int64_t t_first = static_cast<int64_t>(blockIdx.x) * tpw;
+    const int64_t left = T - t_first;
+    const int nt = left <= 0 ? 0 : (left > tpw ? tpw : static_cast<int>(left));
+    const int t0 = nt > 0 ? static_cast<int>(t_first) : 0;
+    const int units = nt * chunks;   // <= kStWaves * kStUnits (the host's choice of tpw)
+    tk::u32x4 res[kStUnits];
 #pragma unroll
-            for (int j = 0; j < K; ++j) {
-                r32[j] = p[j];
-                wj[j] = wt[j];
-            }
-            bool ok[K];
+    for (int i = 0; i < kStUnits; ++i) {
+        res[i] = tk::u32x4{0u, 0u, 0u, 0u};
+        const int u = wave + kStWaves * i;
+        if (u >= units) continue;   // wave-uniform
+        const int tl = u / chunks;
+        const int t = t0 + tl;
+        const int col = (u - tl * chunks) * kChunk + lane * 8;
+        const int32_t* p = pos + static_cast<size_t>(t) * K;
+        const float* wt = w + static_cast<size_t>(t) * K;
+        int32_t r32[K];
+        float wj[K];
 #pragma unroll
-            for (int j = 0; j < K; ++j) ok[j] = r32[j] >= 0 && r32[j] < rows_in && col < H;
-            tk::u32x4 d[K];
+        for (int j = 0; j < K; ++j) {
+            r32[j] = p[j];
+            wj[j] = wt[j];
+        }
+        bool ok[K];
 #pragma unroll
-            for (int j = 0; j < K; ++j) {
-                d[j] = tk::u32x4{0u, 0u, 0u, 0u};
-                if (ok[j]) d[j] = tk::load_stream(y + static_cast<size_t>(r32[j]) * H + col);
-            }
-            float acc[8];
+        for (int j = 0; j < K; ++j) ok[j] = r32[j] >= 0 && r32[j] < rows_in && col < H;
+        tk::u32x4 d[K];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+        for (int j = 0; j < K; ++j) {
+            d[j] = tk::u32x4{0u, 0u, 0u, 0u};
+            if (ok[j]) d[j] = tk::load_stream(y + static_cast<size_t>(r32[j]) * H + col);
+        }
+        float acc[8];
 #pragma unroll
-            for (int j = 0; j < K; ++j) {
-                if (!ok[j]) continue;
-                const uint32_t v[4] = {d[j].x, d[j].y, d[j].z, d[j].w};
+        for (int q = 0; q < 8; ++q) acc[q] = 0.f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    acc[2 * i] = __builtin_fmaf(wj[j], tk::bf16_lo(v[i]), acc[2 * i]);
-                    acc[2 * i + 1] = __builtin_fmaf(wj[j], tk::bf16_hi(v[i]), acc[2 * i + 1]);
-                }
-            }
-            if (col < H) {
-                tk::u32x4 o;
-                o.x = tk::pack_bf16x2(acc[0], acc[1]);
-                o.y = tk::pack_bf16x2(acc[2], acc[3]);
-                o.z = tk::pack_bf16x2(acc[4], acc[5]);
-                o.w = tk::pack_bf16x2(acc[6], acc[7]);
-                *reinterpret_cast<tk::u32x4*>(staged + static_cast<size_t>(tl) * H + col) = o;
+        for (int j = 0; j < K; ++j) {
+            if (!ok[j]) continue;
+            const uint32_t v[4] = {d[j].x, d[j].y, d[j].z, d[j].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[2 * q] = __builtin_fmaf(wj[j], tk::bf16_lo(v[q]), acc[2 * q]);
+                acc[2 * q + 1] = __builtin_fmaf(wj[j], tk::bf16_hi(v[q]), acc[2 * q + 1]);
             }
         }
-        __syncthreads();
-        // rows t0 .. t0 + nt - 1 are contiguous in out: one burst of 16-byte stores
-        const int n16 = nt * (H / 8);
-        uint16_t* dst = out + static_cast<size_t>(t0) * H;
-        for (int i = threadIdx.x; i < n16; i += kStThreads)
-            tk::store_stream(dst + static_cast<size_t>(i) * 8,
-                             *reinterpret_cast<const tk::u32x4*>(staged + static_cast<size_t>(i) * 8));
-        __syncthreads();   // the staged rows are read out before the next tokens
+        res[i].x = tk::pack_bf16x2(acc[0], acc[1]);
+        res[i].y = tk::pack_bf16x2(acc[2], acc[3]);
+        res[i].z = tk::pack_bf16x2(acc[4], acc[5]);
+        res[i].w = tk::pack_bf16x2(acc[6], acc[7]);
+    }
+    __syncthreads();   // every read of the workgroup before any of its stores
+    // rows t0 .. t0 + nt - 1 are contiguous in out; unit u is its 1 KiB at
+    // t * H + chunk * 512, so neighbouring waves store neighbouring pieces
+#pragma unroll
+    for (int i = 0; i < kStUnits; ++i) {
+        const int u = wave + kStWaves * i;
+        if (u >= units) continue;
+        const int tl = u / chunks;
+        const int col = (u - tl * chunks) * kChunk + lane * 8;
+        if (col < H) tk::store_stream(out + static_cast<size_t>(t0 + tl) * H + col, res[i]);
     }
 }
 
-// Tokens per workgroup for the staged form: their rows fit the LDS budget and
-// their units split evenly over the 16 waves; 0 if no such count exists.
-int staged_tokens(int H, int chunks)
+// Tokens per workgroup for the staged form: as many as the waves' unit slots
+// hold (16 waves x 14), at most 16; 0 if one token's row alone has more units.
+int staged_tokens(int chunks)
 {
-    for (int tpw : {8, 4, 2})
-        if (static_cast<int64_t>(tpw) * H * 2 <= kStLdsBytes && (tpw * chunks) % kStWaves == 0)
-            return tpw;
-    return 0;
+    const int tpw = kStWaves * kStUnits / chunks;
+    return tpw < 1 ? 0 : (tpw > kStMaxTokens ? kStMaxTokens : tpw);
 }
 
 // Compute units of the current device (cached per device); 0 if unknown.
@@ -186,38 +186,21 @@ int device_cus(int dev)
     return n > 0 ? n : 0;
 }
 
-// Lets reduce_staged_kernel<K> use kStLdsBytes of LDS on `dev` (once per
-// device); false if the device refuses, and the call then takes the
-// one-wave-per-unit kernel.
-template <int K>
-bool staged_lds_ready(int dev)
-{
-    static std::atomic<bool> ready[kMaxDevices];
-    if (dev < 0 || dev >= kMaxDevices) return false;
-    if (ready[dev].load(std::memory_order_acquire)) return true;
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(reduce_staged_kernel<K>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kStLdsBytes) != hipSuccess) {
-        (void)hipGetLastError();   // not sticky: the fallback launch must not see it
-        return false;
-    }
-    ready[dev].store(true, std::memory_order_release);
-    return true;
-}
-
+// The staged form when it applies: at least one workgroup of tokens per CU
+// (with fewer the chip idles, and the one-wave-per-unit kernel is faster).
 template <int K>
 bool launch_staged(const uint16_t* y, int64_t rows, const int32_t* pos, const float* w, int T,
                    int H, uint16_t* out, hipStream_t stream, hipError_t* e)
 {
     const int chunks = (H + kChunk - 1) / kChunk;
-    const int tpw = staged_tokens(H, chunks);
+    const int tpw = staged_tokens(chunks);
     int dev = -1;
     if (tpw == 0 || hipGetDevice(&dev) != hipSuccess) return false;
     const int cus = device_cus(dev);
     if (cus == 0 || static_cast<int64_t>(T) < static_cast<int64_t>(cus) * tpw) return false;
-    if (!staged_lds_ready<K>(dev)) return false;
     const int64_t groups = (static_cast<int64_t>(T) + tpw - 1) / tpw;
     *e = tk::launch(reduce_staged_kernel<K>, dim3(static_cast<unsigned>(groups)), dim3(kStThreads),
-                    static_cast<size_t>(tpw) * H * 2, stream, y, rows, pos, w, T, H, chunks, tpw, out);
+                    0, stream, y, rows, pos, w, T, H, chunks, tpw, out);
     return true;
 }
 

@@ -212,17 +212,18 @@ def test_reduce_few_tokens(T, k):
     _check_reduce(y, pos, w)
 
 
-# tk_reduce_dense: at T >= (compute units) x (tokens per workgroup) it takes its
-# staged form (a workgroup combines a few consecutive tokens into LDS and
-# writes their rows as one burst); tk_reduce and slices of fewer than 2048
-# tokens take the one-wave-per-unit kernel.  Per token the arithmetic is the
-# same, so all must agree bit for bit; both stay within the combine tolerance
-# of the oracle.  Cases: every compiled k, a ragged last burst, a 520-column
-# row (a partly filled 512-column unit), masked slots and rows beyond y.
-@pytest.mark.parametrize("T,k,H", [(2048, 8, 7168), (4100, 8, 1024), (5000, 6, 2048),
-                                   (3000, 4, 4096), (2600, 2, 520), (2049, 1, 1024),
-                                   (2111, 6, 7168), (3333, 4, 7168), (2047, 8, 7168),
-                                   (2500, 8, 4096)])
+# tk_reduce_dense: at T >= (compute units) x (tokens per workgroup, 16 here) it
+# takes its staged form (a workgroup combines up to 16 consecutive tokens,
+# keeps the results in registers and stores its rows as one burst after a
+# barrier); tk_reduce, slices of 1000 tokens and T just below the threshold
+# take the one-wave-per-unit kernel.  Per token the arithmetic is the same, so
+# all must agree bit for bit; both stay within the combine tolerance of the
+# oracle.  Cases: every compiled k, a ragged last workgroup, a 520-column row
+# (a partly filled 512-column unit), masked slots and rows beyond y.
+@pytest.mark.parametrize("T,k,H", [(4096, 8, 7168), (4100, 8, 1024), (5000, 6, 2048),
+                                   (4500, 4, 4096), (4600, 2, 520), (4097, 1, 1024),
+                                   (4111, 6, 7168), (5333, 4, 7168), (4095, 8, 7168),
+                                   (4500, 8, 4096)])
 def test_reduce_dense_equals_reduce(T, k, H):
     rng = np.random.default_rng(T + 10 * k + H)
     R = T * k
