@@ -223,7 +223,9 @@ def test_reduce_few_tokens(T, k):
 @pytest.mark.parametrize("T,k,H", [(4096, 8, 7168), (4100, 8, 1024), (5000, 6, 2048),
                                    (4500, 4, 4096), (4600, 2, 520), (4097, 1, 1024),
                                    (4111, 6, 7168), (5333, 4, 7168), (4095, 8, 7168),
-                                   (4500, 8, 4096)])
+                                   (4500, 8, 4096),
+                                   # runtime k: the one-wave-per-unit kernel for both
+                                   (4096, 12, 1024), (4200, 32, 520)])
 def test_reduce_dense_equals_reduce(T, k, H):
     rng = np.random.default_rng(T + 10 * k + H)
     R = T * k
