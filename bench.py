@@ -16,13 +16,16 @@ hidden states with 1 % outlier rows x50, bf16 N(0,1) expert outputs) and
 resident in HBM before the timed region.  The expert GEMMs are not part of
 the path: the reduce consumes a fixed expert-output tensor.
 
-Prints ONE JSON line: routed tokens/s (value, back-to-back steps), the
-pipeline's algorithmic HBM GB/s, per-kernel times from HIP events recorded on
-the launch stream (mean, median, p10, p90), the same step with the MALL and
-L2 evicted before each pass (cold_cache), the rate of the repository's
-streaming copy kernel for reference (stream_copy), the roofline of the
-dominant kernel (the reduce) and the CPU oracle's rate (one thread, and
-all host cores on token shards).  Steps beyond the
+Prints ONE JSON line: routed tokens/s (value: passes that each start with
+the MALL and L2 evicted, one pair of HIP events around each), the pipeline's
+algorithmic HBM GB/s, the same passes back to back (warm: x then stays in the
+MALL), per-kernel times from HIP events recorded between the calls (mean,
+median, p10, p90; warm and cold), the rate of the repository's streaming copy
+kernel for reference (stream_copy), the roofline of the dominant kernel (the
+reduce), the CPU oracle's rate (one thread, and all host cores on token
+shards) and the comparison of the step's GPU outputs with the oracle's
+outputs for the same inputs (parity; a mismatch makes the exit status 1).
+Steps beyond the
 routing path (next_rows) are timed separately on the same data and do not
 enter value: SwiGLU + 1x128 FP8 quantisation of the 65536 expanded rows at
 the DeepSeek-V3 expert width I = 2048 (plain and transposing), weighted by the
@@ -97,13 +100,14 @@ def measured_traffic():
         return None
 
 
-def cpu_baseline(inputs, reps: int = 2) -> dict:
+def cpu_baseline(inputs, reps: int = 2):
     """The oracle, as it stands, on full steps of the workload: one thread,
     then all host cores (at most 16).  The all-cores leg calls the same oracle
     functions on token shards from a thread pool -- route, expand and reduce
     are independent per token, and ctypes releases the interpreter lock
     around each C call -- with the map run serially; its outputs are checked
-    equal to the one-thread run's."""
+    equal to the one-thread run's.  Returns the report and the one-thread
+    run's outputs, against which the GPU step's outputs are then compared."""
     import ctypes
     from concurrent.futures import ThreadPoolExecutor
 
@@ -163,18 +167,60 @@ def cpu_baseline(inputs, reps: int = 2) -> dict:
             m_rd += t3 - t2
     same = bool(np.array_equal(idx_m, idx) and np.array_equal(w_m, w) and np.array_equal(pos_m, pos)
                 and np.array_equal(xq_m, xq) and np.array_equal(sc_m, sc) and np.array_equal(out_m, out))
+    del xq_m, sc_m, out_m
     m_secs = (m_rm + m_ex + m_rd) / reps
-    return {"value": round(T / secs, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "host": f"{model}, {os.cpu_count()} logical CPUs visible",
-            "sample": f"{reps} full steps (T={T} each) of route+map+expand(FP8)+reduce through the "
-                      f"single-threaded C oracle, mean per step: route+map {t_rm / reps:.2f}s, "
-                      f"expand {t_ex / reps:.2f}s, reduce {t_rd / reps:.2f}s",
-            "all_cores": {"value": round(T / m_secs, 1), "unit": "tokens/s", "cores": n,
-                          "kind": "oracle", "identical_to_one_thread": same,
-                          "sample": f"the same {reps} steps, the oracle's route, expand and reduce "
-                                    f"on {n} token shards in {n} threads, map serial; mean per "
-                                    f"step: route+map {m_rm / reps:.2f}s, expand {m_ex / reps:.2f}s, "
-                                    f"reduce {m_rd / reps:.2f}s"}}
+    report = {"value": round(T / secs, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+              "host": f"{model}, {os.cpu_count()} logical CPUs visible",
+              "sample": f"{reps} full steps (T={T} each) of route+map+expand(FP8)+reduce through the "
+                        f"single-threaded C oracle, mean per step: route+map {t_rm / reps:.2f}s, "
+                        f"expand {t_ex / reps:.2f}s, reduce {t_rd / reps:.2f}s",
+              "all_cores": {"value": round(T / m_secs, 1), "unit": "tokens/s", "cores": n,
+                            "kind": "oracle", "identical_to_one_thread": same,
+                            "sample": f"the same {reps} steps, the oracle's route, expand and reduce "
+                                      f"on {n} token shards in {n} threads, map serial; mean per "
+                                      f"step: route+map {m_rm / reps:.2f}s, expand {m_ex / reps:.2f}s, "
+                                      f"reduce {m_rd / reps:.2f}s"}}
+    outs = {"idx": idx, "w": w, "counts": counts, "offsets": offsets, "pos": pos,
+            "row_src": row_src, "xq": xq, "sc": sc, "out": out}
+    return report, outs
+
+
+# Parity bars of the step against the oracle: integer and byte outputs
+# bit-exact; weights (fp32 against the oracle's fp64) within W_RTOL; the
+# combine per element within COMBINE_ATOL + COMBINE_RTOL * |ref| in bf16.
+W_RTOL, W_ATOL = 4e-6, 1e-9
+COMBINE_ATOL = COMBINE_RTOL = 1e-2
+
+
+def _bf16_bits_to_f64(h):
+    import numpy as np
+    return (np.ascontiguousarray(h, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def step_parity(gpu: dict, ref: dict) -> dict:
+    """Compare the timed step's GPU outputs with the oracle's outputs for the
+    same inputs (numpy comparisons only)."""
+    import numpy as np
+    exact = {n: bool(np.array_equal(gpu[n], ref[n]))
+             for n in ("idx", "counts", "offsets", "pos", "row_src", "xq", "sc")}
+    w_ok = bool(np.allclose(gpu["w"], ref["w"], rtol=W_RTOL, atol=W_ATOL))
+    w_rel = float(np.max(np.abs(gpu["w"].astype(np.float64) - ref["w"]) /
+                         np.maximum(np.abs(ref["w"]), 1e-30)))
+    g = _bf16_bits_to_f64(gpu["out"])
+    r = _bf16_bits_to_f64(ref["out"])
+    err = np.abs(g - r)
+    ok = err <= COMBINE_ATOL + COMBINE_RTOL * np.abs(r)
+    combine = {"tokens": int(gpu["out"].shape[0]), "allclose": bool(ok.all()),
+               "n_outside": int((~ok).sum()),
+               "max_abs": float(err.max(initial=0.0)),
+               "max_rel": float((err / np.maximum(np.abs(r), 1e-30)).max(initial=0.0)),
+               "bit_exact_frac": float((gpu["out"] == ref["out"]).mean())}
+    return {"ok": all(exact.values()) and w_ok and combine["allclose"],
+            "bit_exact": exact, "weights_within_rtol": w_ok, "weights_max_rel": w_rel,
+            "combine": combine,
+            "bars": f"idx, counts, offsets, pos, row_src, FP8 codes and scales bit-exact; weights "
+                    f"rtol {W_RTOL}; combine |gpu-ref| <= {COMBINE_ATOL} + {COMBINE_RTOL}*|ref| "
+                    f"on every element of the ({T}, {H}) output"}
 
 
 SWIGLU_I = 2048   # DeepSeek-V3's expert width
@@ -556,28 +602,60 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
 
-    # Timed region: exactly `steps` pipeline passes between two events on the
-    # launch stream (torch's current stream, which every tk_* call uses).  No
-    # event sits between the kernels here: on this stream each extra event
-    # record costs a few microseconds of GPU time.
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    # Headline: `steps` passes, each started with the MALL (256 MB) and the
+    # L2s evicted by a 1 GiB read, so no input of the step is cached when it
+    # starts (a read, not a write: a write would leave up to 256 MB of dirty
+    # lines whose write-back the timed step would pay for; the read also
+    # drains the previous pass's own dirty lines).  Each pass is timed by one
+    # pair of HIP events on the launch stream (torch's current stream, which
+    # every tk_* call uses), with the host synchronised before and after; no
+    # event sits between the kernels.
+    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    ev_a = torch.cuda.Event(enable_timing=True)
+    ev_b = torch.cuda.Event(enable_timing=True)
+    cold = []
+    wall0 = time.perf_counter()
+    for _ in range(args.steps):
+        flush.sum()
+        ev_a.record()
+        step()
+        ev_b.record()
+        torch.cuda.synchronize()
+        cold.append(ev_a.elapsed_time(ev_b))
+    wall_cold = time.perf_counter() - wall0
+
+    # Warm: the same number of passes back to back between two events (x
+    # stays in the MALL from one pass to the next, so this is faster).
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t_start.record()
+    ev_a.record()
     for _ in range(args.steps):
         step()
-    t_end.record()
+    ev_b.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_end)
+    wall_warm = time.perf_counter() - wall0
+    warm_ms = ev_a.elapsed_time(ev_b) / args.steps
 
-    # Per-kernel breakdown: the same number of passes again, now with an event
-    # between consecutive calls; the kernel durations (and the roofline of the
-    # dominant kernel) come from this pass.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(evs[i])
+    # Per-kernel breakdown: passes with an event between consecutive calls,
+    # back to back and after a flush; the roofline of the dominant kernel
+    # comes from the back-to-back pass.
+    def breakdown(n, flushed):
+        per = {s: [] for s in steps}
+        for _ in range(n):
+            if flushed:
+                flush.sum()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+            step(ev)
+            if flushed:
+                torch.cuda.synchronize()
+                for j, s in enumerate(steps):
+                    per[s].append(ev[j].elapsed_time(ev[j + 1]))
+            else:
+                evs.append(ev)
+        return per
+
+    evs = []
+    breakdown(args.steps, False)
     torch.cuda.synchronize()
     per = {s: [] for s in steps}
     for e in evs:
@@ -587,25 +665,17 @@ def main() -> int:
     kern_med_us = {s: 1e3 * float(np.median(v)) for s, v in per.items()}
     kern_p10_us = {s: 1e3 * float(np.percentile(v, 10)) for s, v in per.items()}
     kern_p90_us = {s: 1e3 * float(np.percentile(v, 90)) for s, v in per.items()}
-
-    # Cold caches: before each of these passes a 1 GiB read evicts the MALL
-    # (256 MB) and the L2s, so no input of the step is cached when it starts.
-    # A read, not a write: a write would leave up to 256 MB of dirty lines
-    # whose write-back the timed step would pay for; the read also drains the
-    # previous pass's own dirty lines before the timer starts.
-    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
-    cold, cold_per = [], {s: [] for s in steps}
-    for _ in range(min(args.steps, 10)):
-        flush.sum()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
-        step(ev)
-        torch.cuda.synchronize()
-        cold.append(ev[0].elapsed_time(ev[4]))
-        for j, s in enumerate(steps):
-            cold_per[s].append(ev[j].elapsed_time(ev[j + 1]))
-    cold_ms = float(np.median(cold))
+    cold_per = breakdown(min(args.steps, 10), True)
     cold_kern_us = {s: 1e3 * float(np.median(v)) for s, v in cold_per.items()}
     del flush
+
+    # The last flushed pass's outputs, for the comparison with the oracle.
+    step()
+    torch.cuda.synchronize()
+    gpu_out = {"idx": idx.cpu().numpy(), "w": w.cpu().numpy(), "counts": counts.cpu().numpy(),
+               "offsets": offsets.cpu().numpy(), "pos": pos.cpu().numpy(),
+               "row_src": row_src.cpu().numpy(), "xq": xq.cpu().numpy(), "sc": sc.cpu().numpy(),
+               "out": out.view(torch.int16).cpu().numpy().view(np.uint16)}
     copy_gbps = stream_copy_gbps(torch, dev)
 
     if args.calib_copy:
@@ -625,9 +695,10 @@ def main() -> int:
                  **bench_ep_share(tk, torch, np, synth, dev, args.steps),
                  **bench_small_batch(tk, torch, logits, bias, x, y, opts, args.steps)}
 
-    ms_per_step = total_ms / args.steps
+    ms_per_step = float(np.mean(cold))
     value = T / (ms_per_step * 1e-3)
     gbps = BYTES["total"] / (ms_per_step * 1e-3) / 1e9
+    warm_gbps = BYTES["total"] / (warm_ms * 1e-3) / 1e9
     red_s = kern_us["reduce"] * 1e-6
     achieved = BYTES["reduce"] / red_s / 1e9
     traffic = measured_traffic()
@@ -642,45 +713,62 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32",
+        "dtype": "fp32 gating / e4m3 dispatch / bf16 combine (fp32 acc)",
         "data": "synthetic",
         "config": {"workload": WORKLOAD, "T": T, "H": H, "E": E, "k": K, "n_groups": 8,
                    "topk_groups": 4, "route_scale": 2.5, "global_batch": T,
                    "io": "logits fp32, hidden bf16, dispatch E4M3 + fp32 scales, combine bf16",
                    "parallelism": "single GPU"},
+        "timing": "each timed pass starts with the MALL and L2 evicted (1 GiB device read) and "
+                  "is bracketed by one pair of HIP events on the launch stream; value and "
+                  "ms_per_step are the mean over the passes",
         "hbm_gbps": round(gbps, 1),
         "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
+        "hbm_frac_cold": round(gbps / PEAK_HBM_GBPS, 4),
+        "ms_per_step_cold_median": round(float(np.median(cold)), 5),
+        "ms_per_step_cold_p10_p90": [round(float(np.percentile(cold, 10)), 5),
+                                     round(float(np.percentile(cold, 90)), 5)],
         "algorithmic_bytes_per_step": BYTES["total"],
+        "warm": {"ms_per_step": round(warm_ms, 5), "tokens_per_s": round(T / (warm_ms * 1e-3), 1),
+                 "hbm_gbps": round(warm_gbps, 1), "hbm_frac": round(warm_gbps / PEAK_HBM_GBPS, 4),
+                 "timing": "the same passes back to back between two events: x stays in the "
+                           "MALL from one pass to the next"},
         "kernel_us_mean": {s: round(v, 2) for s, v in kern_us.items()},
         "kernel_us_median": {s: round(v, 2) for s, v in kern_med_us.items()},
         "kernel_us_p10": {s: round(v, 2) for s, v in kern_p10_us.items()},
         "kernel_us_p90": {s: round(v, 2) for s, v in kern_p90_us.items()},
-        "cold_cache": {"ms_per_step_median": round(cold_ms, 5), "steps": len(cold),
-                       "kernel_us_median": {s: round(v, 2) for s, v in cold_kern_us.items()},
-                       "hbm_frac": round(BYTES["total"] / (cold_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-                       "flush": "1 GiB device read before each step; events between the calls "
-                                "as in the breakdown pass"},
+        "kernel_us_median_cold": {s: round(v, 2) for s, v in cold_kern_us.items()},
+        "kernel_breakdown": "further passes with an event between calls (each event record "
+                            "adds a few microseconds): back to back, and after a flush (_cold)",
         "stream_copy": None if copy_gbps is None else {
             "gbps": round(copy_gbps, 1),
             "what": "in-repository streaming copy kernel (libtk_calib.so), 1 GiB, read + written "
                     "bytes over time",
-            "pipeline_frac_of_copy": round(gbps / copy_gbps, 4)},
+            "pipeline_frac_of_copy": round(gbps / copy_gbps, 4),
+            "warm_pipeline_frac_of_copy": round(warm_gbps / copy_gbps, 4)},
         "kernel_gbps": {s: round(BYTES[s] / (kern_us[s] * 1e-6) / 1e9, 1) for s in steps},
-        "wall_s_timed": round(wall, 4),
-        "kernel_breakdown": "second pass of the same steps with an event between calls",
+        "wall_s_timed": round(wall_cold, 4),
+        "wall_s_warm": round(wall_warm, 4),
         "roofline": {"kernel": "reduce_staged_kernel<8>", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic,
                      "algorithmic_bytes_per_launch": BYTES["reduce"]},
+        "parity": None,
         "cpu_baseline": None,
         "next_rows": next_rows,
     }
+    rc = 0
     if not args.no_cpu_baseline:
         inputs = (gate["logits"], gate["bias"], x_h, y_h, r)
-        result["cpu_baseline"] = cpu_baseline(inputs)
+        result["cpu_baseline"], ref = cpu_baseline(inputs)
+        result["parity"] = step_parity(gpu_out, ref)
+        rc = 0 if result["parity"]["ok"] else 1
     print(json.dumps(result), flush=True)
-    return 0
+    if rc:
+        print("bench.py: the step's GPU outputs do not match the oracle (see parity)",
+              file=sys.stderr)
+    return rc
 
 
 if __name__ == "__main__":

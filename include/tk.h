@@ -131,9 +131,9 @@ typedef struct tk_route_opts {
  *                the k chosen experts, or the softmax over all E experts
  *                times route_scale when renormalize == 0.
  *
- * logits   device, fp32 (T, E), 4-byte aligned (16-byte aligned if E % 4 == 0
- *          for vector loads)
- * bias     device, fp32 (E) or NULL; sigmoid only
+ * logits   device, fp32 (T, E), 4-byte aligned; 16-byte aligned when E > 128
+ *          and E % 4 == 0 (four experts per lane, read as one vector load)
+ * bias     device, fp32 (E) or NULL; sigmoid only; aligned as logits
  * T        tokens, >= 0
  * E        experts, 1..TK_MAX_EXPERTS
  * k        experts per token, 1..min(E, TK_MAX_TOPK)
@@ -155,7 +155,10 @@ tk_status tk_route(const float* logits, const float* bias, int32_t T, int32_t E,
 size_t tk_map_workspace_bytes(int32_t T, int32_t k, int32_t n_local);
 
 /*
- * tk_map -- token-to-expert mapping with a local-expert mask.
+ * tk_map -- token-to-expert mapping with a local-expert mask: the
+ * "token-to-expert mapping" and "tensor-parallel mask" operations of
+ * TileKernels' moe/ module ("刚刚！DeepSeek开源高性能GPU算子库TileKernels",
+ * item moe/), the mask read as the experts one expert-parallel rank owns.
  *
  * Route (t, j) is local when local_begin <= topk_idx[t,j] < local_end (the
  * experts one expert-parallel rank owns; [0, E) keeps every route).  An
@@ -213,7 +216,11 @@ tk_status tk_map_aligned(const int32_t* topk_idx, int32_t T, int32_t k, int32_t 
 #define TK_EXPAND_FP8_E4M3_1X128 1  /* rows are 1x128-block FP8 E4M3 codes */
 
 /*
- * tk_expand_quant -- gather tokens into expert-contiguous rows.
+ * tk_expand_quant -- gather tokens into expert-contiguous rows: the "fused
+ * expand" of TileKernels' moe/ module with the per-token FP8 quantisation of
+ * its quant/ module fused in ("刚刚！DeepSeek开源高性能GPU算子库TileKernels",
+ * items moe/ and quant/), the FP8 dispatch of the DeepSeek-V3 test shape
+ * ("剛剛，DeepSeek開始頻繁更新：Tile Kernels、DeepEP V2", section 性能表現).
  *
  * For every route with 0 <= pos[t,j] < rows_capacity, row pos[t,j] of `out`
  * receives token t (routes outside that range are skipped).  Each token is
@@ -237,7 +244,10 @@ tk_status tk_expand_quant(const void* x_bf16, int32_t T, int32_t H, int32_t k,
 
 /* ----------------------------------------------------------------- reduce */
 /*
- * tk_reduce -- weighted combine of expert outputs back to tokens.
+ * tk_reduce -- weighted combine of expert outputs back to tokens: the "fused
+ * reduce" of TileKernels' moe/ module ("刚刚！DeepSeek开源高性能GPU算子库
+ * TileKernels", item moe/), the BF16 combine of the DeepSeek-V3 test shape
+ * ("剛剛，DeepSeek開始頻繁更新：Tile Kernels、DeepEP V2", section 性能表現).
  *
  *   out[t, c] = bf16_RNE( fp32 fma chain over j = 0..k-1, in slot order, of
  *               topk_w[t,j] * y[pos[t,j], c] ), starting from +0,

@@ -459,8 +459,9 @@ TK_EXPORT tk_status tk_route(const float* logits, const float* bias, int32_t T, 
     if (!tk::aligned4(logits) || !tk::aligned4(topk_idx) || !tk::aligned4(topk_w) ||
         (bias && !tk::aligned4(bias)))
         return fail(TK_ERR_ARG, "tk_route: fp32/int32 tensors must be 4-byte aligned");
-    if (epl >= 4 && E % 4 == 0 && !tk::aligned16(logits))
-        return fail(TK_ERR_ARG, "tk_route: logits must be 16-byte aligned when E %% 4 == 0");
+    if (epl >= 4 && E % 4 == 0 && (!tk::aligned16(logits) || (bias && !tk::aligned16(bias))))
+        return fail(TK_ERR_ARG,
+                    "tk_route: logits and bias must be 16-byte aligned when E %% 4 == 0 and E > 128");
 
     if (opts->renormalize && epl <= 4 && (opts->n_groups == 1 || opts->group_topn <= 2)) {
         const FastArgs f{logits, bias, topk_idx, topk_w, T, E, opts->n_groups,

@@ -95,6 +95,9 @@ def test_route_rejects_bad_arguments(lib):
     assert _route(lib, 4, 256, 8, RouteOpts(0, 1, 1, 0, 1, 1.0), bias=FAKE) == ARG
     assert _route(lib, 4, 256, 8, o, logits=None) == ARG
     assert _route(lib, 4, 256, 8, o, logits=MIS) == ARG                          # 16B for E%4==0
+    assert _route(lib, 4, 256, 8, o, bias=MIS) == ARG                            # bias likewise
+    assert b"16-byte" in lib.tk_last_error()
+    assert _route(lib, 0, 256, 8, o, logits=None, bias=MIS, idx=None, w=None) == 0
     assert _route(lib, 4, 256, 8, o, idx=MIS1) == ARG
     assert _route(lib, 0, 256, 8, o, logits=None, idx=None, w=None) == 0         # T == 0 no-op
     assert lib.tk_last_error() == b""

@@ -284,12 +284,15 @@ def test_reduce_exact_gather():
     assert np.array_equal(to_host(out), y[perm[:, 0]])
 
 
+@pytest.mark.slow
 @pytest.mark.parametrize("fn", ["tk_reduce", "tk_reduce_dense"])   # the bench's step takes the second
-def test_reduce_v3_full_sampled(fn):
+def test_reduce_v3_full(fn):
+    # the weighted combine at the DeepSeek-V3 shape: expert outputs (65536,
+    # 7168) through the oracle's routing of the v3 gating workload, every one
+    # of the 8192 output tokens compared with the oracle
     cfg = synth.v3_gate(0)
     idx, w = oracle.route(cfg["logits"], cfg["bias"], cfg["k"], **cfg["route"])
     _, offsets, pos, _ = oracle.map_routes(idx, 256)
     y = synth.v3_expert_out(0)
-    sample = np.random.default_rng(35).choice(8192, 256, replace=False)
-    sample = np.concatenate([sample, [0, 8191]])
-    _check_reduce(y, pos, w.astype(np.float32), sample, fn)
+    rep = _check_reduce(y, pos, w.astype(np.float32), None, fn)
+    print(f"{fn} v3 full: {rep}")
