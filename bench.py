@@ -100,6 +100,11 @@ def measured_traffic():
         return None
 
 
+def _progress(msg: str) -> None:
+    """A progress line on stderr (the JSON line alone goes to stdout)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
 def cpu_baseline(inputs, reps: int = 2):
     """The oracle, as it stands, on full steps of the workload: one thread,
     then all host cores (at most 16).  The all-cores leg calls the same oracle
@@ -598,6 +603,7 @@ def main() -> int:
         if ev is not None:
             ev[4].record()
 
+    _progress(f"inputs resident; {args.warmup} warm-up passes")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -623,6 +629,7 @@ def main() -> int:
         torch.cuda.synchronize()
         cold.append(ev_a.elapsed_time(ev_b))
     wall_cold = time.perf_counter() - wall0
+    _progress(f"{args.steps} flushed passes: {sum(cold) / len(cold) * 1e3:.1f} us per pass")
 
     # Warm: the same number of passes back to back between two events (x
     # stays in the MALL from one pass to the next, so this is faster).
@@ -635,6 +642,7 @@ def main() -> int:
     torch.cuda.synchronize()
     wall_warm = time.perf_counter() - wall0
     warm_ms = ev_a.elapsed_time(ev_b) / args.steps
+    _progress(f"{args.steps} back-to-back passes: {warm_ms * 1e3:.1f} us per pass")
 
     # Per-kernel breakdown: passes with an event between consecutive calls,
     # back to back and after a flush; the roofline of the dominant kernel
@@ -686,6 +694,7 @@ def main() -> int:
             b.copy_(a)
         torch.cuda.synchronize()
 
+    _progress("breakdown passes done; timing the next rows")
     next_rows = {"swiglu_quant_fp8": bench_swiglu(tk, torch, y, offsets[E:], row_src, pos, w,
                                                   args.steps),
                  **bench_map_balance(tk, torch, logits, idx, args.steps),
@@ -760,6 +769,7 @@ def main() -> int:
     }
     rc = 0
     if not args.no_cpu_baseline:
+        _progress("next rows done; running the CPU oracle on the step's inputs")
         inputs = (gate["logits"], gate["bias"], x_h, y_h, r)
         result["cpu_baseline"], ref = cpu_baseline(inputs)
         result["parity"] = step_parity(gpu_out, ref)
