@@ -211,6 +211,25 @@ tk_status tk_map_aligned(const int32_t* topk_idx, int32_t T, int32_t k, int32_t 
                          int32_t* offsets, int32_t* pos, int32_t* row_src, void* workspace,
                          size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * tk_map_noalloc -- tk_map for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments minus the workspace, the same checks,
+ * results and errors.  The count matrix lives in a device array of
+ * TK_MAP_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until
+ * the process ends; the call allocates nothing.  Sizes whose workspace
+ * (tk_map_workspace_bytes) exceeds that array return TK_ERR_ARG.  Every call
+ * on one GPU shares that GPU's array: calls that overlap on one GPU (on
+ * concurrent streams, or from several host threads) race and must be
+ * serialised by the caller.  The stream must belong to the current device
+ * (else TK_ERR_ARG); the first call on a device looks the array's address up
+ * there.
+ */
+#define TK_MAP_NOALLOC_SCRATCH_BYTES (1 << 20)
+tk_status tk_map_noalloc(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
+                         int32_t local_begin, int32_t local_end, int32_t* counts,
+                         int32_t* offsets, int32_t* pos, int32_t* row_src, hipStream_t stream);
+
 /* ----------------------------------------------------------------- expand */
 #define TK_EXPAND_BF16 0            /* rows are bitwise copies of the token */
 #define TK_EXPAND_FP8_E4M3_1X128 1  /* rows are 1x128-block FP8 E4M3 codes */

@@ -9,6 +9,7 @@ step of the path runs in the library's HIP kernels; there is no fallback.
     tk_route(logits, bias, k, opts)            -> (topk_idx, topk_w)
     tk_map(topk_idx, E, local_begin, local_end) -> (counts, offsets, pos, row_src)
     tk_map_aligned(topk_idx, E, local_begin, local_end, align) -> (counts, offsets, pos, row_src)
+    tk_map_noalloc(topk_idx, E, local_begin, local_end) -> tk_map without a workspace
     tk_expand_quant(x, pos, mode, rows_capacity) -> (out, scales)
     tk_reduce(y, pos, topk_w)                  -> out
     tk_reduce_dense(y, pos, topk_w)            -> out (the same, dense routings)
@@ -33,6 +34,7 @@ LIB_PATH = os.path.join(_HERE, "libtk.so")
 
 TK_OK, TK_ERR_ARG, TK_ERR_UNSUPPORTED, TK_ERR_DEVICE = 0, -1, -2, -3
 TK_MAX_EXPERTS, TK_MAX_TOPK = 1024, 32
+TK_MAP_NOALLOC_SCRATCH_BYTES = 1 << 20
 TK_SCORE_SOFTMAX, TK_SCORE_SIGMOID = 0, 1
 TK_EXPAND_BF16, TK_EXPAND_FP8_E4M3_1X128 = 0, 1
 (TK_QUANT_FP8_1X128, TK_QUANT_FP8_1X128_POW2, TK_QUANT_FP8_128X128, TK_QUANT_FP8_PER_CHANNEL,
@@ -90,6 +92,8 @@ def library() -> ctypes.CDLL:
         L.tk_map.restype = i32
         L.tk_map_aligned.argtypes = [vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
         L.tk_map_aligned.restype = i32
+        L.tk_map_noalloc.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]
+        L.tk_map_noalloc.restype = i32
         L.tk_expand_quant.argtypes = [vp, i32, i32, i32, vp, i32, vp, vp, i64, vp]
         L.tk_expand_quant.restype = i32
         L.tk_reduce.argtypes = [vp, i64, vp, vp, i32, i32, i32, vp, vp]
@@ -179,6 +183,31 @@ def tk_map(topk_idx: torch.Tensor, E: int, local_begin: int = 0, local_end: int 
            want_row_src: bool = True):
     return tk_map_aligned(topk_idx, E, local_begin, local_end, 1, counts, offsets, pos, row_src,
                           workspace, want_row_src)
+
+
+def tk_map_noalloc(topk_idx: torch.Tensor, E: int, local_begin: int = 0,
+                   local_end: int | None = None, counts=None, offsets=None, pos=None,
+                   row_src=None):
+    """tk_map without a workspace: the count matrix lives in the library's
+    per-GPU array of TK_MAP_NOALLOC_SCRATCH_BYTES.  Outputs the caller does
+    not pass are allocated here (the C call itself allocates nothing)."""
+    _dev(topk_idx, "topk_idx", torch.int32, 2)
+    T, k = topk_idx.shape
+    local_end = E if local_end is None else local_end
+    nl = local_end - local_begin
+    dev = topk_idx.device
+    counts = torch.empty(max(nl, 0), dtype=torch.int32, device=dev) if counts is None else counts
+    offsets = torch.empty(max(nl, 0) + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
+    pos = torch.empty((T, k), dtype=torch.int32, device=dev) if pos is None else pos
+    for name, t, n in (("counts", counts, max(nl, 0)), ("offsets", offsets, max(nl, 0) + 1),
+                       ("pos", pos, T * k)):
+        _dev(t, name, torch.int32, numel=n, device=dev)
+    if row_src is not None:
+        _dev(row_src, "row_src", torch.int32, numel=T * k, device=dev)
+    _check("tk_map_noalloc", library().tk_map_noalloc(
+        _ptr(topk_idx), T, k, E, local_begin, local_end, _ptr(counts), _ptr(offsets),
+        _ptr(pos), _ptr(row_src), _stream(topk_idx)))
+    return counts, offsets, pos, row_src
 
 
 def tk_map_aligned(topk_idx: torch.Tensor, E: int, local_begin: int = 0,

@@ -26,6 +26,8 @@
 // routed to an expert at most once (repeats in a row are dropped).
 // tk_map_aligned pads every expert's segment to a multiple of `align` rows
 // (the layout an M-blocked grouped GEMM reads); tk_map is align = 1.
+#include <mutex>
+
 #include "tk_internal.h"
 
 namespace {
@@ -435,11 +437,13 @@ TK_EXPORT size_t tk_map_workspace_bytes(int32_t T, int32_t k, int32_t n_local)
     return (static_cast<size_t>(g.n_tiles) * n_local + static_cast<size_t>(n_local)) * sizeof(int32_t);
 }
 
-TK_EXPORT tk_status tk_map_aligned(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
-                                   int32_t local_begin, int32_t local_end, int32_t align,
-                                   int32_t* counts, int32_t* offsets, int32_t* pos,
-                                   int32_t* row_src, void* workspace, size_t workspace_bytes,
-                                   hipStream_t stream)
+namespace {
+
+// Host-side argument checks shared by every map entry point (all but the
+// workspace's); TK_OK or the failure status.
+tk_status map_check(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E, int32_t local_begin,
+                    int32_t local_end, int32_t align, const int32_t* counts,
+                    const int32_t* offsets, const int32_t* pos, const int32_t* row_src)
 {
     using tk::fail;
     if (align < 1) return fail(TK_ERR_ARG, "tk_map: align=%d < 1", align);
@@ -459,15 +463,30 @@ TK_EXPORT tk_status tk_map_aligned(const int32_t* topk_idx, int32_t T, int32_t k
         return fail(TK_ERR_ARG, "tk_map: NULL counts/offsets");
     if (T > 0 && (topk_idx == nullptr || pos == nullptr))
         return fail(TK_ERR_ARG, "tk_map: NULL topk_idx/pos");
+    if (!tk::aligned4(counts) || !tk::aligned4(offsets) || (pos && !tk::aligned4(pos)) ||
+        (row_src && !tk::aligned4(row_src)) || (topk_idx && !tk::aligned4(topk_idx)))
+        return fail(TK_ERR_ARG, "tk_map: int32 tensors must be 4-byte aligned");
+    return TK_OK;
+}
+
+}  // namespace
+
+TK_EXPORT tk_status tk_map_aligned(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
+                                   int32_t local_begin, int32_t local_end, int32_t align,
+                                   int32_t* counts, int32_t* offsets, int32_t* pos,
+                                   int32_t* row_src, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream)
+{
+    using tk::fail;
+    const tk_status st = map_check(topk_idx, T, k, E, local_begin, local_end, align, counts,
+                                   offsets, pos, row_src);
+    if (st != TK_OK) return st;
     const int nl = local_end - local_begin;
     const size_t need = tk_map_workspace_bytes(T, k, nl);
     if (workspace_bytes < need)
         return fail(TK_ERR_ARG, "tk_map: workspace of %zu bytes < %zu needed", workspace_bytes, need);
     if (need > 0 && (workspace == nullptr || !tk::aligned16(workspace)))
         return fail(TK_ERR_ARG, "tk_map: workspace NULL or not 16-byte aligned");
-    if (!tk::aligned4(counts) || !tk::aligned4(offsets) || (pos && !tk::aligned4(pos)) ||
-        (row_src && !tk::aligned4(row_src)) || (topk_idx && !tk::aligned4(topk_idx)))
-        return fail(TK_ERR_ARG, "tk_map: int32 tensors must be 4-byte aligned");
 
     hipError_t e;
     if (T == 0) {
@@ -516,4 +535,71 @@ TK_EXPORT tk_status tk_map(const int32_t* topk_idx, int32_t T, int32_t k, int32_
 {
     return tk_map_aligned(topk_idx, T, k, E, local_begin, local_end, 1, counts, offsets, pos,
                           row_src, workspace, workspace_bytes, stream);
+}
+
+// ------------------------------------------------------------ no allocation
+// tk_map_noalloc: tk_map with its count matrix in a fixed device array
+// instead of a caller-provided workspace.  Each GPU the library runs on holds
+// its own copy of the array (TK_MAP_NOALLOC_SCRATCH_BYTES) until the process
+// ends.  In host code `scratch` names a host-side stand-in, not the device
+// array, so kernels receive the address hipGetSymbolAddress returns, looked
+// up once per device with that device current.  The map overwrites every
+// count it later reads, so nothing in the array needs clearing between calls.
+static __device__ __align__(256) int32_t scratch[TK_MAP_NOALLOC_SCRATCH_BYTES / sizeof(int32_t)];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's device address on device `dev` (the current device),
+// looked up on the first call there; or an error status.
+tk_status scratch_on_device(int dev, void** out)
+{
+    if (dev < 0 || dev >= kMaxDevices)
+        return tk::fail(TK_ERR_UNSUPPORTED, "tk_map_noalloc: device %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return tk::fail(TK_ERR_DEVICE, "tk_map_noalloc: hipGetSymbolAddress: %s",
+                            hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return TK_OK;
+}
+
+}  // namespace
+
+TK_EXPORT tk_status tk_map_noalloc(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
+                                   int32_t local_begin, int32_t local_end, int32_t* counts,
+                                   int32_t* offsets, int32_t* pos, int32_t* row_src,
+                                   hipStream_t stream)
+{
+    using tk::fail;
+    tk_status st = map_check(topk_idx, T, k, E, local_begin, local_end, 1, counts, offsets, pos,
+                             row_src);
+    if (st != TK_OK) return st;
+    const size_t need = tk_map_workspace_bytes(T, k, local_end - local_begin);
+    if (need > TK_MAP_NOALLOC_SCRATCH_BYTES)
+        return fail(TK_ERR_ARG,
+                    "tk_map_noalloc: T=%d with %d local experts needs %zu bytes of scratch, more "
+                    "than the %d the library holds; use tk_map with a workspace",
+                    T, local_end - local_begin, need, TK_MAP_NOALLOC_SCRATCH_BYTES);
+    int dev = -1, stream_dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipStreamGetDevice(stream, &stream_dev);
+    if (e != hipSuccess)
+        return fail(TK_ERR_DEVICE, "tk_map_noalloc: device query: %s", hipGetErrorString(e));
+    if (stream_dev != dev)
+        return fail(TK_ERR_ARG, "tk_map_noalloc: stream is on device %d, current device is %d",
+                    stream_dev, dev);
+    void* ws = nullptr;
+    st = scratch_on_device(dev, &ws);
+    if (st != TK_OK) return st;
+    return tk_map_aligned(topk_idx, T, k, E, local_begin, local_end, 1, counts, offsets, pos,
+                          row_src, ws, TK_MAP_NOALLOC_SCRATCH_BYTES, stream);
 }

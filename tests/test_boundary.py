@@ -32,7 +32,7 @@ def lib():
     for name in ("tk_route", "tk_map", "tk_map_aligned", "tk_expand_quant", "tk_reduce",
                  "tk_reduce_dense", "tk_expert_standin", "tk_swiglu_quant", "tk_swiglu_quant_t",
                                   "tk_silu_bf16", "tk_balance_loss",
-                 "tk_quant"):
+                 "tk_quant", "tk_map_noalloc"):
         getattr(L, name).restype = ctypes.c_int32
     L.tk_map_workspace_bytes.restype = ctypes.c_size_t
     L.tk_balance_workspace_bytes.restype = ctypes.c_size_t
@@ -46,7 +46,7 @@ def test_header_declares_the_entry_points():
                                   "tk_reduce_dense", "tk_expert_standin", "tk_swiglu_quant", "tk_swiglu_quant_t",
                                   "tk_silu_bf16",
                                   "tk_balance_workspace_bytes", "tk_balance_loss",
-                                  "tk_quant_workspace_bytes", "tk_quant"])
+                                  "tk_quant_workspace_bytes", "tk_quant", "tk_map_noalloc"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -123,6 +123,27 @@ def test_map_rejects_bad_arguments(lib):
     assert _map(lib, 4, 8, 256, 0, 256, ws=MIS1) == ARG
     assert _map(lib, 4, 8, 256, 0, 256, ws=MIS) == ARG     # workspace needs 16-byte alignment
     assert _map(lib, 4, 8, 256, 0, 256, idx=None) == ARG
+
+
+def test_map_noalloc_rejects_bad_arguments_and_sizes(lib):
+    # the argument checks of tk_map, then the size of the library's scratch
+    # array, all before any device call (these run without a GPU)
+    I = ctypes.c_int32
+
+    def call(T, k, E, lo, hi, counts=FAKE, idx=FAKE, pos=FAKE):
+        return lib.tk_map_noalloc(idx, I(T), I(k), I(E), I(lo), I(hi), counts, FAKE, pos, None,
+                                  None)
+    assert call(-1, 8, 256, 0, 256) == ARG
+    assert call(4, 0, 256, 0, 256) == ARG
+    assert call(4, 33, 256, 0, 256) == UNSUP
+    assert call(4, 8, 256, 32, 32) == ARG
+    assert call(4, 8, 256, 0, 256, counts=None) == ARG
+    assert call(4, 8, 256, 0, 256, idx=MIS1) == ARG
+    # 1 MiB holds the count matrix up to T*n_local/256 + n_local ints = 2^18
+    assert lib.tk_map_workspace_bytes(261120, 8, 256) <= 1 << 20
+    assert call(262144, 8, 256, 0, 256) == ARG
+    assert b"scratch" in lib.tk_last_error()
+    assert call(200000, 8, 1024, 0, 1024) == ARG
 
 
 def test_map_workspace_bytes(lib):
