@@ -136,6 +136,11 @@ def test_map_v3_gate_full():
     (1, 8, 1, 0, 8), (31, 16, 2, 0, 16), (1000, 256, 8, 32, 64), (4097, 256, 8, 0, 256),
     (777, 64, 3, 0, 64), (300, 1024, 32, 0, 1024), (512, 1024, 9, 100, 900),
     (2049, 32, 4, 7, 8), (5000, 160, 6, 0, 160), (70000, 256, 8, 0, 256),
+    # count + place with the per-tile counts summed in place (small count
+    # matrix: a masked range, or 64 experts) or scanned in a third launch
+    # (more than 32768 counts), around 2^18 routes
+    (32768, 256, 8, 0, 256), (32769, 256, 8, 0, 256), (40000, 256, 8, 32, 64),
+    (33000, 64, 8, 0, 64),
     # one tile (the single-launch map): a full 256-token tile, a masked range,
     # 1024 experts (128-token tiles) with k = 32, the tiny softmax shape
     (256, 256, 8, 0, 256), (200, 64, 5, 10, 50), (128, 1024, 32, 0, 1024), (64, 16, 2, 0, 16),
@@ -146,7 +151,7 @@ def test_map_random_routing(T, E, k, lo, hi):
     _assert_map(idx, E, lo, hi)
 
 
-@pytest.mark.parametrize("T", [600, 100])   # three tiles; one tile
+@pytest.mark.parametrize("T", [600, 100, 40000])   # three tiles; one tile; two launches
 def test_map_repeats_and_out_of_range_ids(T):
     rng = np.random.default_rng(7)
     E, k = 32, 6
@@ -184,6 +189,7 @@ def test_map_deterministic():
     (4097, 256, 8, 0, 256, 128), (777, 64, 3, 0, 64, 7), (2049, 32, 4, 7, 8, 1000),
     (70000, 256, 8, 0, 256, 64), (300, 1024, 32, 0, 1024, 16),
     (200, 256, 8, 0, 256, 128), (100, 1024, 32, 0, 1024, 16), (64, 64, 4, 8, 40, 3),
+    (40000, 64, 8, 0, 64, 128), (33000, 256, 8, 0, 256, 32),
 ])
 def test_map_aligned_random_routing(T, E, k, lo, hi, align):
     rng = np.random.default_rng(T + E + align)

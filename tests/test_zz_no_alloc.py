@@ -36,13 +36,13 @@ def _noalloc(idx, E, lo, hi):
 
 
 def test_map_noalloc_matches_map_twice():
-    cases = []
-    g = synth.v3_gate(0)                                     # T=8192, E=256, k=8, no mask
-    o_idx, _ = oracle.route(g["logits"], g["bias"], g["k"], **g["route"])
-    cases.append((o_idx, 256, 0, 256))
+    # both calls run the count pass into the scratch array: the first through
+    # the separate scan (T=40000, 256 experts: more than 32768 counts), the
+    # second, smaller one with a local-expert mask summing the per-tile counts
+    # in the place pass
     rng = np.random.default_rng(5)
-    small = synth.random_routing(rng, 1000, 64, 6)           # smaller, masked to [16, 48)
-    cases.append((small, 64, 16, 48))
+    cases = [(synth.random_routing(rng, 40000, 256, 8), 256, 0, 256),
+             (synth.random_routing(rng, 33000, 64, 8), 64, 16, 48)]
     for idx_h, E, lo, hi in cases:
         idx = to_dev(idx_h)
         got = _noalloc(idx, E, lo, hi)
