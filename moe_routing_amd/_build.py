@@ -5,7 +5,10 @@ writes _build/sigmoid_table.inc, the pinned sigmoid at every bf16 value of
 its band, which swiglu.hip includes.  Then each .hip source is compiled to an
 object under _build/ in parallel and linked into moe_routing_amd/libtk.so;
 calib.hip (a streaming copy bench.py measures for reference) becomes
-moe_routing_amd/libtk_calib.so.
+moe_routing_amd/libtk_calib.so.  build_asan() builds the same library with
+AddressSanitizer on the host side only (argument checks, error state, launch
+wrappers; the device code is built as usual) into _build/asan/, for the CPU
+test that runs the boundary checks under the ASan runtime.
 Always recompiles (a build check must compile); callers that only need the
 library load it when it exists.
 """
@@ -52,9 +55,25 @@ def _sigmoid_table() -> None:
         raise RuntimeError(f"sigmoid_table_gen failed:\n{r.stdout}\n{r.stderr}")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+ASAN_DIR = os.path.join(BUILD, "asan")
+ASAN_LIB = os.path.join(ASAN_DIR, "libtk_host_asan.so")
+# AddressSanitizer for the host code only: each -fsanitize= goes to the host
+# compilation (-Xarch_host), never to the gfx950 device code.
+ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer",
+              "-Xarch_host", "-g"]
+
+
+def asan_runtime() -> str | None:
+    """Path of the compiler's shared ASan runtime, or None."""
+    r = subprocess.run([HIPCC, "--print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True)
+    path = r.stdout.strip()
+    return path if r.returncode == 0 and os.path.isabs(path) and os.path.exists(path) else None
+
+
+def _compile(src: str, out_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
@@ -82,6 +101,26 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print(f"built {LIB} and {CALIB_LIB}")
     return LIB
+
+
+def build_asan(verbose: bool = False) -> str:
+    """libtk with AddressSanitizer on the host code, in _build/asan/ (not loaded
+    by the package; the ASan CPU test loads it under the ASan runtime)."""
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    if not os.path.exists(os.path.join(BUILD, "sigmoid_table.inc")):
+        _sigmoid_table()
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(lambda src: _compile(src, ASAN_DIR, ASAN_FLAGS), SOURCES))
+    tmp = ASAN_LIB + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *ASAN_FLAGS,
+           "-Xarch_host", "-shared-libasan", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed (asan):\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, ASAN_LIB)
+    if verbose:
+        print(f"built {ASAN_LIB}")
+    return ASAN_LIB
 
 
 if __name__ == "__main__":

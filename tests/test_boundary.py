@@ -11,7 +11,9 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "tk.h")
-LIB = os.path.join(ROOT, "moe_routing_amd", "libtk.so")
+# TK_BOUNDARY_LIB: another build of the same library to check (the ASan test
+# runs this file against the host-sanitised build)
+LIB = os.environ.get("TK_BOUNDARY_LIB") or os.path.join(ROOT, "moe_routing_amd", "libtk.so")
 
 ARG, UNSUP = -1, -2
 
