@@ -22,9 +22,9 @@
 // workgroup's.
 
 // Quotient x/scale: Markstein's correction on the reciprocal,
-//   inv = RN(1/scale); q0 = RN(x*inv); r = fma(-q0, scale, x); q = fma(r, inv, q0)
-// (P. Markstein, IBM J. Res. Dev. 34(1), 1990), with the sign of x restored
-// for x = -0.  It equals the IEEE quotient RN(x/scale) for every (x, scale)
+//   inv = RN(1/scale); q0 = RN(x*inv); rn = fma(q0, scale, -x); q = fma(-rn, inv, q0)
+// (P. Markstein, IBM J. Res. Dev. 34(1), 1990; the residual is negated so
+// that x = -0 keeps its sign).  It equals the IEEE quotient RN(x/scale) for every (x, scale)
 // this kernel can see, except where both lie below 2^-10 and so encode to the
 // same signed zero; tests/test_quotient_domain.py enumerates that domain.
 // FP8 encoding: gfx950's v_cvt_pk_fp8_f32 (OCP E4M3FN, round to nearest even).

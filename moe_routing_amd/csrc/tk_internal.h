@@ -205,18 +205,20 @@ __host__ __device__ __forceinline__ float pinned_sigmoid(float x) { return 1.0f 
 
 // -------------------------------------------------- 1x128 E4M3 codec
 // x / scale for scale > 0 by Markstein's correction on the correctly rounded
-// reciprocal inv = RN(1/scale): q0 = RN(x*inv); r = fma(-q0, scale, x) (exact);
+// reciprocal inv = RN(1/scale): q0 = RN(x*inv); r = x - q0*scale (exact);
 // q = RN(q0 + r*inv) is the correctly rounded quotient (P. Markstein, IBM J.
 // Res. Dev. 34(1), 1990; Muller et al., Handbook of Floating-Point
 // Arithmetic).  Quotients that underflow encode to a signed E4M3 zero either
-// way.  The correction step maps x = -0 to +0 (the sum +0 + -0 rounds to +0),
-// so the sign of x is put back; for x != 0 the sign is already right and
-// copysign changes nothing.
+// way.  The residual is formed negated, rn = fma(q0, scale, -x) = -r (RN is
+// symmetric), and applied as fma(-rn, inv, q0): three instructions with the
+// negations as operand modifiers.  For x = -0 that keeps the sign (q0 = -0,
+// rn = +0, and -0 + -0 = -0), where fma(r, inv, q0) with r = +0 would give
+// +0 and need the sign put back.
 __device__ __forceinline__ float fp8_quotient(float x, float scale, float inv)
 {
     const float q0 = x * inv;
-    const float r = __builtin_fmaf(-q0, scale, x);
-    return __builtin_copysignf(__builtin_fmaf(r, inv, q0), x);
+    const float rn = __builtin_fmaf(q0, scale, -x);
+    return __builtin_fmaf(-rn, inv, q0);
 }
 
 // Four quotients -> four E4M3 codes (gfx950 hardware convert: OCP E4M3FN,

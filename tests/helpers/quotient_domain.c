@@ -1,12 +1,12 @@
 /*
  * Exhaustive check, on the host, of the division shortcut the FP8 expand
  * kernel uses for q = x / scale:
- *     inv = RN(1/scale); q0 = RN(x*inv); r = fma(-q0, scale, x); q = fma(r, inv, q0)
- * (Markstein's correction step).  The domain is every pair the kernel can
+ *     inv = RN(1/scale); q0 = RN(x*inv); rn = fma(q0, scale, -x); q = fma(-rn, inv, q0)
+ * (Markstein's correction step, with the residual negated so that x = -0
+ * keeps its sign).  The domain is every pair the kernel can
  * see: amax = a bf16 magnitude >= 1e-4 or the clamp value 1e-4f,
  * scale = RN(amax/448), and x = every bf16 value with |x| <= amax, both
- * signs (-0 included: the correction step alone would turn it into +0, so
- * the kernel restores the sign of x).  For each pair the
+ * signs (-0 included).  For each pair the
  * shortcut must equal the IEEE quotient RN(x/scale) bit for bit, except where
  * both lie below 2^-10 -- half the smallest E4M3 subnormal, so both encode to
  * the same signed zero.  (Differences occur only for x tiny against a huge
@@ -36,8 +36,11 @@ static long long check_amax(float amax, long long* pairs, long long* tiny)
         const float x = f32(h << 16);
         if (!(fabsf(x) <= amax)) continue;
         const float q0 = x * inv;
-        const float r = fmaf(-q0, scale, x);
-        const float q = copysignf(fmaf(r, inv, q0), x);
+        const float rn = fmaf(q0, scale, -x);
+        /* -rn by its sign bit, as the kernel's negation modifier: a compiler
+           may not turn -fma(a, b, c) into fma(-a, b, -c), which differs for
+           a zero result */
+        const float q = fmaf(f32(bits(rn) ^ 0x80000000u), inv, q0);
         const float ref = x / scale;
         if (bits(q) != bits(ref)) {
             if (fabsf(q) < kTiny && fabsf(ref) < kTiny && signbit(q) == signbit(ref)) {

@@ -1,6 +1,7 @@
 """Host proof of the FP8 expand kernel's division shortcut.
 
-The kernel replaces x/scale by Markstein's correction of x*RN(1/scale).  The
+The kernel replaces x/scale by Markstein's correction of x*RN(1/scale),
+with the residual formed negated so that x = -0 keeps its sign.  The
 helper enumerates every (x, scale) pair the kernel can see -- scale from every
 bf16 block maximum >= 1e-4 (and the 1e-4 clamp), x every bf16 value up to
 that maximum -- and requires the shortcut to equal the IEEE quotient bit for
