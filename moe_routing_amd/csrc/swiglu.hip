@@ -249,39 +249,10 @@ constexpr int kTRows = 4;                         // rows per thread
 constexpr int kTGroups = kTile / kTRows;          // 32 row groups
 constexpr int kTPitch = kTile + 16;               // bytes per staged out_t row (padded)
 static_assert(kTRows == 4, "a row group's rows are handed out by quad broadcasts");
-// Tiles are dealt out by XCD.  The dispatcher hands workgroups to the eight
-// XCDs in turn (workgroup b runs on XCD b % 8), and XCD x takes whole
-// super-blocks of kSBRows row tiles by all column tiles (super-blocks x,
-// x + 8, ...), each in row-major tile order, so workgroups running side by
-// side read whole rows of h.  Every 4-byte scale store then shares its
-// 64-byte line only with stores from the same XCD: a row's scales (one per
-// column tile) and a column's transposed scales (one per row tile of a
-// super-block).  That XCD's L2 merges them into whole lines before they
-// reach HBM, instead of eight L2s each writing back a partial line.  (The
-// assignment is a performance choice only; any dispatch order gives the
-// same results.)
-constexpr int kXcds = 8;
-constexpr int kSBRows = 16;                       // row tiles per super-block: 16 scales a line
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-struct TileOrder {
-    int64_t n_tr;   // row tiles
-    int tiles_c;    // column tiles
-    int xcd;        // this workgroup's XCD (0 when the grid is not dealt by XCD)
-    int xcds;       // XCDs the super-blocks are dealt to (1 or kXcds)
-};
-
-// The j-th tile of this workgroup's XCD -> (row tile, column tile); false
-// once j is past the XCD's last tile (tiles only grow with j).
-__device__ __forceinline__ bool tile_of(int64_t j, const TileOrder& o, int64_t& tr, int& tc)
-{
-    const int64_t sb_tiles = static_cast<int64_t>(kSBRows) * o.tiles_c;
-    const int64_t sb = (j / sb_tiles) * o.xcds + o.xcd;
-    const int64_t w = j % sb_tiles;
-    tr = sb * kSBRows + w / o.tiles_c;
-    tc = static_cast<int>(w % o.tiles_c);
-    return tr < o.n_tr;
-}
+// Tile t -> (row tile, column tile): the column tiles of one row tile are
+// consecutive, so workgroups running side by side read whole rows of h.
+__device__ __forceinline__ int64_t tile_row(int64_t t, int tiles_c) { return t / tiles_c; }
+__device__ __forceinline__ int tile_col(int64_t t, int tiles_c) { return static_cast<int>(t % tiles_c); }
 
 // lane i of each lane quad, to all four lanes (DPP quad_perm [i,i,i,i]); i is
 // a compile-time constant after unrolling
@@ -356,22 +327,9 @@ void swiglu_quant_t_kernel(SwigluArgs a, int64_t tiles, uint8_t* __restrict__ ou
         bits |= tk::dpp_u32<tk::kQuadXor2>(bits);
         if (wsub == 0) w_row[wrow] = __uint_as_float(bits);
     };
-    // this workgroup's tiles: j = first, first + step, ... of its XCD's list.
-    // Dealt by XCD only when every XCD gets at least four super-blocks (the
-    // last one may be partial), so that no XCD idles while another works on.
-    const int64_t n_sb = (R / kTile + kSBRows - 1) / kSBRows;
-    const bool by_xcd = gridDim.x % kXcds == 0 && n_sb >= 4 * kXcds;
-    const TileOrder order{R / kTile, tiles_c, by_xcd ? static_cast<int>(blockIdx.x % kXcds) : 0,
-                          by_xcd ? kXcds : 1};
-    const int64_t first = by_xcd ? blockIdx.x / kXcds : blockIdx.x;
-    const int64_t step = by_xcd ? gridDim.x / kXcds : gridDim.x;
-    (void)tiles;
-    int64_t tr;
-    int tc;
-    bool have = tile_of(first, order, tr, tc);
     if constexpr (WEIGHTED) {
-        if (have) {
-            const int64_t row = tr * kTile + wrow;
+        if (blockIdx.x < tiles) {
+            const int64_t row = tile_row(blockIdx.x, tiles_c) * kTile + wrow;
             const int t = a.row_src[row];
             load_slots(t);
             pick_weight(t, row);
@@ -379,13 +337,13 @@ void swiglu_quant_t_kernel(SwigluArgs a, int64_t tiles, uint8_t* __restrict__ ou
     }
     __syncthreads();   // the table and the first tile's weights
 
-    for (int64_t j = first; have; j += step) {
+    for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+        const int64_t tr = tile_row(tile, tiles_c);
+        const int tc = tile_col(tile, tiles_c);
         const int64_t r0 = tr * kTile;
         const int c0 = tc * kTile;
-        int64_t tr_next;
-        int tc_next;
-        const bool has_next = tile_of(j + step, order, tr_next, tc_next);
-        const int64_t next_row = tr_next * kTile + wrow;
+        const int64_t next = tile + gridDim.x;
+        const int64_t next_row = tile_row(next, tiles_c) * kTile + wrow;
 
         tk::u32x4 gw[kTRows], uw[kTRows];
 #pragma unroll
@@ -396,7 +354,7 @@ void swiglu_quant_t_kernel(SwigluArgs a, int64_t tiles, uint8_t* __restrict__ ou
         }
         int tok_next = -1;
         if constexpr (WEIGHTED) {
-            if (has_next) tok_next = a.row_src[next_row];
+            if (next < tiles) tok_next = a.row_src[next_row];
         }
 
         float v[kTRows][8];
@@ -462,8 +420,7 @@ void swiglu_quant_t_kernel(SwigluArgs a, int64_t tiles, uint8_t* __restrict__ ou
             o.y = tk::pack_fp8x4(tk::fp8_quotient(v[i][4], scale, inv), tk::fp8_quotient(v[i][5], scale, inv),
                                  tk::fp8_quotient(v[i][6], scale, inv), tk::fp8_quotient(v[i][7], scale, inv));
             const int64_t r = r0 + rg * kTRows + i;
-            __builtin_nontemporal_store(
-                u32x2{o.x, o.y}, reinterpret_cast<u32x2*>(a.out + static_cast<size_t>(r) * a.I + c0 + cg * 8));
+            *reinterpret_cast<uint2*>(a.out + static_cast<size_t>(r) * a.I + c0 + cg * 8) = o;
             if (cg == 0) a.scales[static_cast<size_t>(r) * (a.I / 128) + tc] = scale;
         }
 
@@ -497,12 +454,9 @@ void swiglu_quant_t_kernel(SwigluArgs a, int64_t tiles, uint8_t* __restrict__ ou
             tk::store_stream(out_t + static_cast<size_t>(c0 + c) * R + r0 + part * 16, q);
         }
         if constexpr (WEIGHTED) {
-            if (has_next) pick_weight(tok_next, next_row);
+            if (next < tiles) pick_weight(tok_next, next_row);
         }
         __syncthreads();   // stage read out before the next tile; its weights published
-        tr = tr_next;
-        tc = tc_next;
-        have = has_next;
     }
 }
 
