@@ -151,6 +151,20 @@ def test_expand_bf16(T, E, k, H):
     assert np.array_equal(to_host(out), ref)
 
 
+def test_expand_bf16_v3_full():
+    # the expand without quantisation at the bench's shape: every one of the
+    # 65536 rows a bitwise copy of its token
+    cfg = synth.v3_gate(0)
+    idx, _ = oracle.route(cfg["logits"], cfg["bias"], cfg["k"], **cfg["route"])
+    _, offsets, pos, _ = oracle.map_routes(idx, 256)
+    x = synth.v3_hidden(0)
+    R = int(offsets[-1])
+    out, _ = tk.tk_expand_quant(to_dev(x, bf16=True), to_dev(pos), tk.TK_EXPAND_BF16, R)
+    torch.cuda.synchronize()
+    ref, _ = oracle.expand(x, pos, 0, R)
+    assert np.array_equal(to_host(out), ref)
+
+
 def test_expand_zero_tokens():
     x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
     pos = torch.empty((0, 2), dtype=torch.int32, device="cuda")
