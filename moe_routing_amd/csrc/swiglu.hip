@@ -249,10 +249,25 @@ constexpr int kTRows = 4;                         // rows per thread
 constexpr int kTGroups = kTile / kTRows;          // 32 row groups
 constexpr int kTPitch = kTile + 16;               // bytes per staged out_t row (padded)
 static_assert(kTRows == 4, "a row group's rows are handed out by quad broadcasts");
-// Tile t -> (row tile, column tile): the column tiles of one row tile are
-// consecutive, so workgroups running side by side read whole rows of h.
-__device__ __forceinline__ int64_t tile_row(int64_t t, int tiles_c) { return t / tiles_c; }
-__device__ __forceinline__ int tile_col(int64_t t, int tiles_c) { return static_cast<int>(t % tiles_c); }
+// Tile t = (row tile) * tiles_c + (column tile): the column tiles of one row
+// tile are consecutive, so workgroups running side by side read whole rows of
+// h.  A workgroup's tiles are t, t + G, t + 2G, ... (G workgroups); the step
+// moves (row tile, column tile) by (G / tiles_c, G % tiles_c) with a carry,
+// so the loop divides nothing (a 64-bit division is over a hundred scalar
+// instructions).
+struct TileCursor {
+    int64_t tr;
+    int tc;
+    __device__ __forceinline__ void advance(int64_t step_r, int step_c, int tiles_c)
+    {
+        tr += step_r;
+        tc += step_c;
+        if (tc >= tiles_c) {
+            tc -= tiles_c;
+            ++tr;
+        }
+    }
+};
 
 // lane i of each lane quad, to all four lanes (DPP quad_perm [i,i,i,i]); i is
 // a compile-time constant after unrolling
@@ -266,12 +281,13 @@ __device__ __forceinline__ float quad_lane(float x, int i)
     }
 }
 
-constexpr int kTBlocks = 768;                     // 3 per CU of a 256-CU device
+constexpr int kTBlocks = 512;                     // 2 per CU of a 256-CU device
 
-// (6 waves per SIMD is what the LDS allows: three workgroups per CU; the
-// register budget is held to it)
+// (5 waves per SIMD, two workgroups per CU: the weighted form needs about 94
+// VGPRs.  Held to the 80 that six waves allow -- three workgroups per CU,
+// the LDS limit -- it spilled loop values to scratch and ran slower.)
 template <bool WEIGHTED>
-__global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(6)))
+__global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(5)))
 void swiglu_quant_t_kernel(SwigluArgs a, int64_t tiles, uint8_t* __restrict__ out_t,
                            float* __restrict__ scales_t)
 {
@@ -327,9 +343,12 @@ void swiglu_quant_t_kernel(SwigluArgs a, int64_t tiles, uint8_t* __restrict__ ou
         bits |= tk::dpp_u32<tk::kQuadXor2>(bits);
         if (wsub == 0) w_row[wrow] = __uint_as_float(bits);
     };
+    const int64_t step_r = gridDim.x / tiles_c;
+    const int step_c = static_cast<int>(gridDim.x % tiles_c);
+    TileCursor cur{blockIdx.x / tiles_c, static_cast<int>(blockIdx.x % tiles_c)};
     if constexpr (WEIGHTED) {
         if (blockIdx.x < tiles) {
-            const int64_t row = tile_row(blockIdx.x, tiles_c) * kTile + wrow;
+            const int64_t row = cur.tr * kTile + wrow;
             const int t = a.row_src[row];
             load_slots(t);
             pick_weight(t, row);
@@ -338,12 +357,13 @@ void swiglu_quant_t_kernel(SwigluArgs a, int64_t tiles, uint8_t* __restrict__ ou
     __syncthreads();   // the table and the first tile's weights
 
     for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
-        const int64_t tr = tile_row(tile, tiles_c);
-        const int tc = tile_col(tile, tiles_c);
+        const int64_t tr = cur.tr;
+        const int tc = cur.tc;
         const int64_t r0 = tr * kTile;
         const int c0 = tc * kTile;
         const int64_t next = tile + gridDim.x;
-        const int64_t next_row = tile_row(next, tiles_c) * kTile + wrow;
+        cur.advance(step_r, step_c, tiles_c);   // the next tile's coordinates
+        const int64_t next_row = cur.tr * kTile + wrow;
 
         tk::u32x4 gw[kTRows], uw[kTRows];
 #pragma unroll
