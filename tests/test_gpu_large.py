@@ -1,4 +1,4 @@
-"""GPU parity past 4 GiB: the routing step and the SwiGLU at T = 76800 tokens,
+"""GPU parity past 4 GiB: the routing step, the SwiGLU and the codecs at T = 76800 tokens,
 H = 7168, E = 256, k = 8 (R = 614,400 expanded rows).  The FP8 expand writes
 4.4 GB, the bf16 expand and the combine's input y are 8.8 GB and the SwiGLU
 reads 5.0 GB, so their byte offsets pass 2^32 and need 64-bit arithmetic.
@@ -155,4 +155,26 @@ def test_large_swiglu_both_layouts(big):
         assert np.array_equal(to_host(qt[:, r0:r1]), qt_ref), f"transposed codes, block {b}"
         assert np.array_equal(to_host(st[:, b:b + 1]), st_ref), f"transposed scales, block {b}"
     del h, q, s, qt, st, q2, s2
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("mode_name", ["TK_QUANT_FP8_1X128", "TK_QUANT_FP8_1X128_POW2",
+                                       "TK_QUANT_FP8_128X128", "TK_QUANT_FP4_1X32"])
+def test_large_quant_modes(big, mode_name):
+    """The codec granularities whose blocks are local to a row or a 128-row
+    block, over an 8.8 GB matrix (per-channel scales need every row and are
+    covered at the hidden-state shape)."""
+    dev, mode = big["dev"], getattr(tk, mode_name)
+    x = _gpu_bf16((R, H), 14, dev)
+    q, sc = tk.tk_quant(x, mode)
+    torch.cuda.synchronize()
+    n_blk = R // 128
+    blocks = sorted({0, n_blk - 1, *big["rng"].choice(n_blk, 2, replace=False).tolist()})
+    for b in blocks:
+        r0, r1 = 128 * b, 128 * b + 128
+        q_ref, s_ref = oracle.quant(_bits(x[r0:r1]), mode)
+        assert np.array_equal(to_host(q[r0:r1]), q_ref), f"codes, block {b}"
+        g_s = to_host(sc[b:b + 1]) if mode == tk.TK_QUANT_FP8_128X128 else to_host(sc[r0:r1])
+        assert np.array_equal(g_s, s_ref), f"scales, block {b}"
+    del x, q, sc
     torch.cuda.empty_cache()
