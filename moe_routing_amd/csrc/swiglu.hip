@@ -240,7 +240,10 @@ __global__ __launch_bounds__(tk::kBlock) void silu_kernel(const uint16_t* __rest
 // waves per SIMD): a row's 128 columns live in 16 consecutive lanes (DPP row
 // max), a column's 128 rows in 32 row groups across the eight waves (LDS
 // max).  The transposed codes are staged in LDS and leave as whole 16-byte
-// pieces of out_t's rows.  The grid is persistent (at most kTBlocks
+// pieces of out_t's rows.  The LDS layouts keep the lanes of one instruction on
+// different banks: a staged row's 16-byte slots are rotated per column group,
+// the column scales are stored transposed and the column partial maxima padded
+// (each of these was a 4- to 16-way bank conflict, about 3 % of the time).  The grid is persistent (at most kTBlocks
 // workgroups, each striding over the tiles), so the sigmoid table is copied
 // once per workgroup.
 constexpr int kTile = 128;
@@ -298,7 +301,9 @@ void swiglu_quant_t_kernel(SwigluArgs a, int64_t tiles, uint8_t* __restrict__ ou
     // the column partial maxima, then (once they are reduced) the staged codes
     __shared__ __align__(16) uint8_t stage[kTile * kTPitch];
     static_assert(sizeof(float) * kTGroups * kTile <= kTile * kTPitch, "stage too small");
-    auto col_part = reinterpret_cast<float (*)[kTile]>(stage);
+    constexpr int kPartPitch = kTile + 4;   // padded: the row groups' writes fall on different banks
+    static_assert(sizeof(float) * kTGroups * kPartPitch <= kTile * kTPitch, "stage too small");
+    auto col_part = reinterpret_cast<float (*)[kPartPitch]>(stage);
     load_sigmoid_table<kTThreads>(sig);
 
     const int tiles_c = a.I / kTile;
@@ -451,26 +456,33 @@ void swiglu_quant_t_kernel(SwigluArgs a, int64_t tiles, uint8_t* __restrict__ ou
 #pragma unroll
             for (int g = 1; g < kTGroups; ++g) m = fmaxf(m, col_part[g][threadIdx.x]);
             const float scale = fmaxf(m, 1e-4f) / 448.0f;
-            col_scale[threadIdx.x] = scale;
-            col_inv[threadIdx.x] = 1.0f / scale;
+            // stored transposed (column c at (c % 8) * 16 + c / 8): a thread's eight columns
+            // cg*8 .. cg*8+7 are then read at j*16 + cg, sixteen distinct banks per read
+            const int ti = (threadIdx.x & 7) * 16 + (threadIdx.x >> 3);
+            col_scale[ti] = scale;
+            col_inv[ti] = 1.0f / scale;
             scales_t[static_cast<size_t>(c0 + threadIdx.x) * (R / kTile) + tr] = scale;
         }
         __syncthreads();   // col_scale ready, col_part consumed: stage now holds codes
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const float scale = col_scale[cg * 8 + j], inv = col_inv[cg * 8 + j];
+            const float scale = col_scale[j * 16 + cg], inv = col_inv[j * 16 + cg];
             const uint32_t q = tk::pack_fp8x4(tk::fp8_quotient(v[0][j], scale, inv),
                                               tk::fp8_quotient(v[1][j], scale, inv),
                                               tk::fp8_quotient(v[2][j], scale, inv),
                                               tk::fp8_quotient(v[3][j], scale, inv));
-            *reinterpret_cast<uint32_t*>(stage + (cg * 8 + j) * kTPitch + rg * kTRows) = q;
+            // 16-byte slot (rg / 4) of the column's staged row, rotated by cg & 7 so that the
+            // lanes of one store instruction spread over the LDS banks
+            const int slot = (rg >> 2) ^ (cg & 7);
+            *reinterpret_cast<uint32_t*>(stage + (cg * 8 + j) * kTPitch + slot * 16 + (rg & 3) * 4) = q;
         }
         if constexpr (WEIGHTED) load_slots(tok_next);   // the next tile's slots
         __syncthreads();
         // 128 out_t rows of 128 bytes: 8 threads per row, 16 bytes each
         for (int i = threadIdx.x; i < kTile * 8; i += kTThreads) {
             const int c = i >> 3, part = i & 7;
-            const tk::u32x4 q = *reinterpret_cast<const tk::u32x4*>(stage + c * kTPitch + part * 16);
+            const int slot = part ^ ((c >> 3) & 7);
+            const tk::u32x4 q = *reinterpret_cast<const tk::u32x4*>(stage + c * kTPitch + slot * 16);
             tk::store_stream(out_t + static_cast<size_t>(c0 + c) * R + r0 + part * 16, q);
         }
         if constexpr (WEIGHTED) {
