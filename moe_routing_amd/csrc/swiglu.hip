@@ -236,14 +236,14 @@ __global__ __launch_bounds__(tk::kBlock) void silu_kernel(const uint16_t* __rest
 // with 1x128 blocks along each row (the tile's 128 columns), and the
 // transpose a^T with 1x128 blocks along each of its rows (the tile's 128 rows
 // of one column).  Thread (rg, cg) = (tid / 16, tid % 16) holds rows 4*rg..
-// and columns 8*cg.. of the tile (32 values, few enough registers for six
-// waves per SIMD): a row's 128 columns live in 16 consecutive lanes (DPP row
-// max), a column's 128 rows in 32 row groups across the eight waves (LDS
-// max).  The transposed codes are staged in LDS and leave as whole 16-byte
-// pieces of out_t's rows.  The LDS layouts keep the lanes of one instruction on
-// different banks: a staged row's 16-byte slots are rotated per column group,
-// the column scales are stored transposed and the column partial maxima padded
-// (each of these was a 4- to 16-way bank conflict, about 3 % of the time).  The grid is persistent (at most kTBlocks
+// and columns 8*cg.. of the tile (32 values): a row's 128 columns live in 16
+// consecutive lanes (DPP row max), a column's 128 rows in 32 row groups across
+// the eight waves (LDS max).  The transposed codes are staged in LDS and leave
+// as whole 16-byte pieces of out_t's rows.  The LDS layouts keep the lanes of
+// one instruction on different banks: a staged row's 16-byte slots are
+// rotated per column group, the column scales are stored transposed and the
+// column partial maxima padded (each of these was a 4- to 16-way bank
+// conflict, about 3 % of the time).  The grid is persistent (at most kTBlocks
 // workgroups, each striding over the tiles), so the sigmoid table is copied
 // once per workgroup.
 constexpr int kTile = 128;
