@@ -111,6 +111,36 @@ def _map(lib, T, k, E, lo, hi, ws_bytes=1 << 20, counts=FAKE, ws=FAKE, idx=FAKE,
                       ctypes.c_size_t(ws_bytes), None)
 
 
+def test_last_error_is_per_thread(lib):
+    # eight host threads fail tk_route with their own E at the same time (ctypes
+    # drops the GIL inside the call); each must read back its own message, and
+    # a successful call on a thread clears only that thread's text
+    import threading
+    opts = RouteOpts(1, 1, 1, 0, 1, 1.0)
+    bad = []
+
+    def worker(i):
+        E = TK_MAX_EXPERTS_PLUS + i
+        for n in range(500):
+            if _route(lib, 4, E, 2, opts) != UNSUP or f"E={E} ".encode() not in lib.tk_last_error():
+                bad.append((i, n, lib.tk_last_error()))
+                return
+            if n % 50 == 0:
+                if _route(lib, 0, 64, 2, opts) != 0 or lib.tk_last_error() != b"":
+                    bad.append((i, n, "clear", lib.tk_last_error()))
+                    return
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not bad, bad[:3]
+
+
+TK_MAX_EXPERTS_PLUS = 1025     # one past TK_MAX_EXPERTS
+
+
 def test_map_rejects_bad_arguments(lib):
     assert _map(lib, -1, 8, 256, 0, 256) == ARG
     assert _map(lib, 4, 0, 256, 0, 256) == ARG
