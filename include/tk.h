@@ -37,8 +37,8 @@
  * for the expert computation in end-to-end tests.
  *
  * The operations are the ones the pages list for TileKernels' moe/ module --
- * "top-k gating, expert scoring, token-to-expert mapping, fused
- * expand/reduce, tensor-parallel mask" ("刚刚！DeepSeek开源高性能GPU算子库
+ * top-k gating and expert scoring, the token-to-expert mapping, the fused
+ * expand and reduce, and the tensor-parallel mask ("刚刚！DeepSeek开源高性能GPU算子库
  * TileKernels", item moe/; "剛剛，DeepSeek開始頻繁更新：Tile Kernels、DeepEP V2",
  * feature list) -- with per-token FP8 quantisation from the quant/ module
  * (same pages) fused into the expand, at the DeepSeek-V3 shape with FP8
@@ -156,7 +156,7 @@ size_t tk_map_workspace_bytes(int32_t T, int32_t k, int32_t n_local);
 
 /*
  * tk_map -- token-to-expert mapping with a local-expert mask: the
- * "token-to-expert mapping" and "tensor-parallel mask" operations of
+ * token-to-expert mapping and tensor-parallel mask operations of
  * TileKernels' moe/ module ("刚刚！DeepSeek开源高性能GPU算子库TileKernels",
  * item moe/), the mask read as the experts one expert-parallel rank owns.
  *
@@ -193,7 +193,7 @@ tk_status tk_map(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
  * tk_map_aligned -- tk_map with every expert's segment padded for an
  * M-blocked grouped GEMM (the expert-contiguous layout a grouped GEMM such as
  * DeepGEMM's m-grouped kernel reads, "DeepSeek 的 GPU 内核帝国…", section
- * 第二层：DeepGEMM, kernel list; the "new GEMM layout" of DeepEP V2 in
+ * 第二层：DeepGEMM, kernel list; the new GEMM layout of DeepEP V2 in
  * "剛剛，DeepSeek開始頻繁更新：Tile Kernels、DeepEP V2", EPv2 features):
  *   offsets[0] = 0, offsets[e+1] = offsets[e] + roundup(counts[e], align)
  *   pos[t,j]   = offsets[e] + number of tokens t' < t routed to e (or -1)
@@ -235,8 +235,8 @@ tk_status tk_map_noalloc(const int32_t* topk_idx, int32_t T, int32_t k, int32_t 
 #define TK_EXPAND_FP8_E4M3_1X128 1  /* rows are 1x128-block FP8 E4M3 codes */
 
 /*
- * tk_expand_quant -- gather tokens into expert-contiguous rows: the "fused
- * expand" of TileKernels' moe/ module with the per-token FP8 quantisation of
+ * tk_expand_quant -- gather tokens into expert-contiguous rows: the fused
+ * expand of TileKernels' moe/ module with the per-token FP8 quantisation of
  * its quant/ module fused in ("刚刚！DeepSeek开源高性能GPU算子库TileKernels",
  * items moe/ and quant/), the FP8 dispatch of the DeepSeek-V3 test shape
  * ("剛剛，DeepSeek開始頻繁更新：Tile Kernels、DeepEP V2", section 性能表現).
@@ -263,8 +263,8 @@ tk_status tk_expand_quant(const void* x_bf16, int32_t T, int32_t H, int32_t k,
 
 /* ----------------------------------------------------------------- reduce */
 /*
- * tk_reduce -- weighted combine of expert outputs back to tokens: the "fused
- * reduce" of TileKernels' moe/ module ("刚刚！DeepSeek开源高性能GPU算子库
+ * tk_reduce -- weighted combine of expert outputs back to tokens: the fused
+ * reduce of TileKernels' moe/ module ("刚刚！DeepSeek开源高性能GPU算子库
  * TileKernels", item moe/), the BF16 combine of the DeepSeek-V3 test shape
  * ("剛剛，DeepSeek開始頻繁更新：Tile Kernels、DeepEP V2", section 性能表現).
  *
@@ -388,7 +388,7 @@ size_t tk_balance_workspace_bytes(int32_t T, int32_t E);
 
 /*
  * tk_balance_loss -- per-expert load statistics and the load-balance loss of
- * one batch: the "load-balancing loss computation" of TileKernels' moe/
+ * one batch: the load-balancing loss computation of TileKernels' moe/
  * module ("刚刚！DeepSeek开源高性能GPU算子库TileKernels", item moe/), in the form
  * DeepSeek-V3 trains with:
  *   count_e = number of (t, j) with topk_idx[t,j] = e (ids outside [0,E) ignored)
@@ -415,7 +415,7 @@ tk_status tk_balance_loss(const float* logits, const int32_t* topk_idx, int32_t 
 /*
  * tk_swiglu_quant -- SwiGLU activation fused with per-token 1x128 FP8 E4M3
  * quantisation of expert rows, optionally applying each row's routing weight:
- * the "SwiGLU + FP8 quantisation" fusion of TileKernels' quant/ module
+ * the SwiGLU and FP8 quantisation fusion of TileKernels' quant/ module
  * ("刚刚！DeepSeek开源高性能GPU算子库TileKernels", item quant/; "剛剛，DeepSeek
  * 開始頻繁更新：Tile Kernels、DeepEP V2", feature list) and the weighted
  * SwiGLU-to-FP8 helper of the DeepGEMM kernel list ("DeepSeek 的 GPU 内核帝国…",

@@ -1,5 +1,5 @@
 // tk_balance_loss: per-expert load statistics and the load-balance loss of
-// one batch -- the "load-balancing loss computation" of TileKernels' moe/
+// one batch -- the load-balancing loss computation of TileKernels' moe/
 // module ("刚刚！DeepSeek开源高性能GPU算子库TileKernels", item moe/), in the form
 // DeepSeek-V3 trains with:
 //   count_e = routes (t, j) with topk_idx[t,j] = e;  f_e = E/(k*T) * count_e

@@ -1,6 +1,6 @@
 // tk_expand_quant: expand tokens into expert-contiguous rows, optionally with
-// fused per-token 1x128 FP8 E4M3 quantisation ("fused expand" of TileKernels'
-// moe/ module and "per-token FP8" of its quant/ module, "刚刚！DeepSeek开源高性能
+// fused per-token 1x128 FP8 E4M3 quantisation (the fused expand of TileKernels'
+// moe/ module and the per-token FP8 of its quant/ module, "刚刚！DeepSeek开源高性能
 // GPU算子库TileKernels", items moe/ and quant/; FP8 dispatch at the DeepSeek-V3
 // shape, "剛剛，DeepSeek開始頻繁更新：Tile Kernels、DeepEP V2", section 性能表現).
 // Also tk_expert_standin, the dequantise-and-scale harness kernel.

@@ -1,5 +1,5 @@
 // tk_map: token-to-expert mapping (counts, offsets, stable positions) with a
-// local-expert mask; the "token-to-expert mapping" and "tensor-parallel mask"
+// local-expert mask; the token-to-expert mapping and tensor-parallel mask
 // ops of TileKernels' moe/ module ("刚刚！DeepSeek开源高性能GPU算子库TileKernels",
 // item moe/).
 //

@@ -1,4 +1,4 @@
-// tk_reduce: weighted combine of expert outputs back to tokens ("fused reduce"
+// tk_reduce: weighted combine of expert outputs back to tokens (the fused reduce
 // of TileKernels' moe/ module, "刚刚！DeepSeek开源高性能GPU算子库TileKernels",
 // item moe/; BF16 combine at the DeepSeek-V3 shape, "剛剛，DeepSeek開始頻繁更新：
 // Tile Kernels、DeepEP V2", section 性能表現).

@@ -1,6 +1,6 @@
 // tk_swiglu_quant: SwiGLU activation fused with per-token 1x128 FP8 E4M3
 // quantisation, optionally applying each expanded row's routing weight --
-// the "SwiGLU + FP8 quantisation" fusion of TileKernels' quant/ module
+// the SwiGLU and FP8 quantisation fusion of TileKernels' quant/ module
 // ("刚刚！DeepSeek开源高性能GPU算子库TileKernels", item quant/: SwiGLU activation,
 // FP8 quantisation and transpose done in one pass instead of three HBM round
 // trips; "剛剛，DeepSeek開始頻繁更新：Tile Kernels、DeepEP V2", feature list), and

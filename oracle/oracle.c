@@ -300,7 +300,7 @@ int orc_route(const float* logits, const float* bias, int T, int E, int k,
 
 /* ------------------------------------------------------------------------ */
 /* Load-balance statistics and loss over one batch of T tokens (the          */
-/* "load-balancing loss computation" of TileKernels' moe/ module), in the    */
+/* load-balancing loss computation of TileKernels' moe/ module), in the      */
 /* form DeepSeek-V3 trains with:                                             */
 /*   count_e = number of routes (t, j) with topk_idx[t,j] = e                 */
 /*   f_e     = E / (k T) * count_e            (1 for a perfectly even load)   */
@@ -587,7 +587,7 @@ void orc_row_weights(const int32_t* pos, const float* w, int T, int k, int64_t r
 
 /* ------------------------------------------------------------------------ */
 /* SwiGLU activation fused with per-token 1x128 FP8 quantisation (the        */
-/* "SwiGLU + FP8 quantisation" fusion of TileKernels' quant/ module), with   */
+/* SwiGLU and FP8 quantisation fusion of TileKernels' quant/ module), with   */
 /* an optional per-row weight (the routing weight of the expanded row).      */
 /* Row r of h holds 2*I bf16 values: gate g = h[r, 0..I), up u = h[r, I..2I).*/
 /* In fp32, one IEEE operation per step:                                     */
