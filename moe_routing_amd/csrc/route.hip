@@ -466,7 +466,9 @@ TK_EXPORT tk_status tk_route(const float* logits, const float* bias, int32_t T, 
     if (opts->renormalize && epl <= 4 && (opts->n_groups == 1 || opts->group_topn <= 2)) {
         const FastArgs f{logits, bias, topk_idx, topk_w, T, E, opts->n_groups,
                          opts->topk_groups, opts->group_topn, lpg, opts->route_scale};
-        const dim3 grid(static_cast<unsigned>((static_cast<int64_t>(T) + tk::kWavesPerBlock - 1) / tk::kWavesPerBlock)), block(tk::kBlock);
+        const dim3 grid(static_cast<unsigned>((static_cast<int64_t>(T) + tk::kWavesPerBlock - 1) /
+                                              tk::kWavesPerBlock)),
+            block(tk::kBlock);
         const bool sig = opts->score == TK_SCORE_SIGMOID;
         hipError_t e = hipErrorInvalidValue;
         bool launched = true;
@@ -507,7 +509,9 @@ TK_EXPORT tk_status tk_route(const float* logits, const float* bias, int32_t T, 
     RouteArgs a{logits, bias, topk_idx, topk_w, T, E, k,
                 opts->score, opts->n_groups, opts->topk_groups, opts->group_topn,
                 opts->renormalize ? 1 : 0, lpg, opts->route_scale};
-    const dim3 grid(static_cast<unsigned>((static_cast<int64_t>(T) + tk::kWavesPerBlock - 1) / tk::kWavesPerBlock)), block(tk::kBlock);
+    const dim3 grid(static_cast<unsigned>((static_cast<int64_t>(T) + tk::kWavesPerBlock - 1) /
+                                          tk::kWavesPerBlock)),
+        block(tk::kBlock);
     hipError_t e;
     switch (epl) {
     case 1: e = tk::launch(route_kernel<1>, grid, block, 0, stream, a); break;
