@@ -206,7 +206,7 @@ TK_EXPORT tk_status tk_balance_loss(const float* logits, const int32_t* topk_idx
     if (!tk::aligned4(logits) || !tk::aligned4(topk_idx) || !tk::aligned4(f) ||
         !tk::aligned4(P) || !tk::aligned4(loss) || !tk::aligned4(workspace))
         return fail(TK_ERR_ARG, "tk_balance_loss: tensors must be 4-byte aligned");
-    const int n_tiles = (T + kTileTokens - 1) / kTileTokens;
+    const int n_tiles = static_cast<int>((static_cast<int64_t>(T) + kTileTokens - 1) / kTileTokens);
     float* part_p = static_cast<float*>(workspace);
     int32_t* part_c = reinterpret_cast<int32_t*>(part_p + static_cast<size_t>(n_tiles) * E);
     auto* done = reinterpret_cast<uint32_t*>(part_c + static_cast<size_t>(n_tiles) * E);

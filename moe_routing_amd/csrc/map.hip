@@ -52,10 +52,10 @@ __host__ inline Tiling tiling(int T, int n_local)
     Tiling g{};
     int s_max = (kLdsWords - 3 * n_local) / (2 * n_local);  // mask + before words per tile
     s_max = s_max < 1 ? 1 : (s_max > kMaxSub ? kMaxSub : s_max);
-    const int s = (T + kSub - 1) / kSub;                 // no more sub-tiles than tokens need
-    g.S = s < 1 ? 1 : (s > s_max ? s_max : s);
+    const int64_t s = (static_cast<int64_t>(T) + kSub - 1) / kSub;   // no more sub-tiles than tokens need
+    g.S = s < 1 ? 1 : (s > s_max ? s_max : static_cast<int>(s));
     g.tile = g.S * kSub;
-    g.n_tiles = T > 0 ? (T + g.tile - 1) / g.tile : 0;
+    g.n_tiles = T > 0 ? static_cast<int>((static_cast<int64_t>(T) + g.tile - 1) / g.tile) : 0;
     g.fused = static_cast<int64_t>(g.n_tiles) * n_local <= kMaxFusedInts;
     return g;
 }
