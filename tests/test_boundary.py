@@ -186,6 +186,10 @@ def test_map_workspace_bytes(lib):
     assert f(8192, 8, 256) == (32 * 256 + 256) * 4     # 32 tiles of 256 tokens
     assert f(32768, 8, 32) == (128 * 32 + 32) * 4      # 128 tiles of 256 tokens
     assert f(1, 1, 1024) == (1 * 1024 + 1024) * 4      # one tile
+    # the largest T the int32 positions allow (k = 1): tile counts in 64 bits
+    big = 2**31 - 1
+    assert f(big, 1, 256) == ((big + 255) // 256 * 256 + 256) * 4
+    assert lib.tk_balance_workspace_bytes(big, 256) > 0
 
 
 def _expand(lib, T, H, k, mode, cap, x=FAKE, out=FAKE, scales=FAKE, pos=FAKE):
