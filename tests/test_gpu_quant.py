@@ -110,7 +110,7 @@ _ALIGN = {tk.TK_QUANT_FP8_1X128: 128, tk.TK_QUANT_FP8_1X128_POW2: 128,
           tk.TK_QUANT_FP8_128X128: 128, tk.TK_QUANT_FP8_PER_CHANNEL: 8, tk.TK_QUANT_FP4_1X32: 32}
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(32))
 def test_quant_sweep(seed):
     """Seeded random shapes: any mode, 1..600 rows, columns any allowed multiple up to 4096."""
     rng = np.random.default_rng(7000 + seed)
