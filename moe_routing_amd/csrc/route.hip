@@ -406,6 +406,186 @@ __global__ __launch_bounds__(tk::kBlock) void route_fast_kernel(FastArgs a)
     }
 }
 
+// ------------------------------------------------------- two tokens per wave
+// For many tokens (the grid then holds more waves than the SIMDs can run at
+// once and the kernel is bound by VALU issue): the fast kernel's selection
+// for 128 < E <= 256 (E a multiple of 8) with two tokens per wave -- lanes
+// [0, 32) hold one token, lanes [32, 64) the next, eight experts per lane.
+// The cross-lane work (group top-2 butterflies, the group ranking, the k
+// rounds of max + ballot) then serves two tokens per instruction; the
+// lane-local work (scores, the sort of eight keys) costs the same per token.
+// A round's maximum over a half is four DPP steps within 16-lane rows and one
+// row exchange (v_permlane16_swap swaps rows 0 and 1, 2 and 3), which leaves
+// each half's maximum in all of its lanes.  With fewer tokens the longer
+// per-wave instruction stream is not hidden and the one-token kernel is
+// faster, so the host takes this form from kHalfMinTokens on.
+constexpr int kHalfMinTokens = 12288;
+
+__device__ __forceinline__ uint32_t max_half_u32(uint32_t v)
+{
+    v = max(v, tk::dpp_u32<tk::kQuadXor1>(v));
+    v = max(v, tk::dpp_u32<tk::kQuadXor2>(v));
+    v = max(v, tk::dpp_u32<tk::kHalfMirror>(v));
+    v = max(v, tk::dpp_u32<tk::kMirror>(v));
+    const auto sw = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return max(static_cast<uint32_t>(sw[0]), static_cast<uint32_t>(sw[1]));
+}
+
+template <int K, bool SIGMOID>
+__global__ __launch_bounds__(tk::kBlock) void route_half_kernel(FastArgs a)
+{
+    constexpr int EPL = 8;
+    const int lane = threadIdx.x & (tk::kWave - 1);
+    const int half = lane >> 5, hl = lane & 31;
+    const int t0 = 2 * (blockIdx.x * tk::kWavesPerBlock + tk::uniform(threadIdx.x / tk::kWave));
+    if (t0 >= a.T) return;
+    const int t = t0 + half;
+    const bool live = t < a.T;                 // the last wave's second token may not exist
+    const float* row = a.logits + static_cast<size_t>(live ? t : t0) * a.E;
+    const int e0 = hl * EPL;
+    const bool has_bias = a.bias != nullptr;
+
+    float x[EPL], b[EPL];
+    {
+        float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0, w0 = v0, w1 = v0;
+        if (e0 < a.E) {
+            v0 = *reinterpret_cast<const float4*>(row + e0);
+            v1 = *reinterpret_cast<const float4*>(row + e0 + 4);
+            if (has_bias) {
+                w0 = *reinterpret_cast<const float4*>(a.bias + e0);
+                w1 = *reinterpret_cast<const float4*>(a.bias + e0 + 4);
+            }
+        }
+        x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
+        x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
+        b[0] = w0.x; b[1] = w0.y; b[2] = w0.z; b[3] = w0.w;
+        b[4] = w1.x; b[5] = w1.y; b[6] = w1.z; b[7] = w1.w;
+    }
+    const bool mine = live && e0 < a.E;
+    float sc[EPL];
+    uint32_t key[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        float kf;
+        if constexpr (SIGMOID) {
+            sc[i] = tk::pinned_sigmoid(x[i]);
+            kf = has_bias ? sc[i] + b[i] : sc[i];
+        } else {
+            sc[i] = x[i];
+            kf = x[i];
+        }
+        key[i] = mine ? order_key(kf) : 0u;
+    }
+
+    // group limit: groups are runs of lpg lanes inside a half
+    if (a.n_groups > 1) {
+        uint32_t m1 = 0, m2 = 0;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            m2 = max(m2, min(m1, key[i]));
+            m1 = max(m1, key[i]);
+        }
+        const int lpg = a.lanes_per_group;
+        if (lpg >= 2) merge_top2_dpp<tk::kQuadXor1>(m1, m2);
+        if (lpg >= 4) merge_top2_dpp<tk::kQuadXor2>(m1, m2);
+        if (lpg >= 8) merge_top2_dpp<tk::kHalfMirror>(m1, m2);
+        if (lpg >= 16) merge_top2_dpp<tk::kMirror>(m1, m2);
+        const float gs = (a.group_topn == 2) ? key_value(m1) + key_value(m2) : key_value(m1);
+        const uint32_t og = order_key(gs);
+        // lane i of group g compares g with groups i, i + lpg, ...; a ballot
+        // over the group's lanes counts the groups that beat g
+        const int g = hl / lpg, i = hl & (lpg - 1);
+        const uint64_t seg = ((1ull << lpg) - 1ull) << (lane & ~(lpg - 1));
+        int rank = 0;
+        for (int gp0 = 0; gp0 < a.n_groups; gp0 += lpg) {
+            const int gp = gp0 + i;
+            const bool real = gp < a.n_groups;
+            const uint32_t o = static_cast<uint32_t>(
+                __shfl(static_cast<int>(og), (half << 5) + (real ? gp : 0) * lpg));
+            const bool beats = real && (o > og || (o == og && gp < g));
+            rank += __popcll(__ballot(beats) & seg);
+        }
+        if (rank >= a.topk_groups) {
+#pragma unroll
+            for (int i2 = 0; i2 < EPL; ++i2) key[i2] = 0;
+        }
+    }
+
+    // the lane's eight keys sorted descending as (key << 32 | 7 - i)
+    // composites (equal keys keep the lower expert first), by a 19-comparator
+    // network; then split into keys and a packed list of 3-bit local indices,
+    // head in the low bits
+    uint32_t lk[EPL];
+    uint32_t li_packed = 0;
+    {
+        uint64_t c[EPL];
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) c[i] = (static_cast<uint64_t>(key[i]) << 32) | (EPL - 1 - i);
+        cas_desc(c[0], c[2]); cas_desc(c[1], c[3]); cas_desc(c[4], c[6]); cas_desc(c[5], c[7]);
+        cas_desc(c[0], c[4]); cas_desc(c[1], c[5]); cas_desc(c[2], c[6]); cas_desc(c[3], c[7]);
+        cas_desc(c[0], c[1]); cas_desc(c[2], c[3]); cas_desc(c[4], c[5]); cas_desc(c[6], c[7]);
+        cas_desc(c[2], c[4]); cas_desc(c[3], c[5]);
+        cas_desc(c[1], c[4]); cas_desc(c[3], c[6]);
+        cas_desc(c[1], c[2]); cas_desc(c[3], c[4]); cas_desc(c[5], c[6]);
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            lk[i] = static_cast<uint32_t>(c[i] >> 32);
+            li_packed |= (EPL - 1 - static_cast<uint32_t>(c[i] & 7u)) << (3 * i);
+        }
+    }
+
+    // k rounds: each half's maximum head, the lowest lane of the half that
+    // holds it (a ballot split in two), and a pop of that lane's list
+    int my_e = 0;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        const uint32_t m = max_half_u32(lk[0]);
+        const uint64_t won = __ballot(lk[0] == m);
+        // each half has a lane at its maximum, so neither half of the ballot is 0
+        const int wl0 = tk::uniform(__builtin_ctz(static_cast<uint32_t>(won)));
+        const int wl1 = 32 + tk::uniform(__builtin_ctz(static_cast<uint32_t>(won >> 32)));
+        const int li0 = readlane_i(static_cast<int>(li_packed & 7u), wl0);
+        const int li1 = readlane_i(static_cast<int>(li_packed & 7u), wl1);
+        const int e = half ? (wl1 - 32) * EPL + li1 : wl0 * EPL + li0;
+        if (hl == j) my_e = e;
+        if (lane == wl0 || lane == wl1) {
+#pragma unroll
+            for (int i = 0; i + 1 < EPL; ++i) lk[i] = lk[i + 1];
+            lk[EPL - 1] = 0;
+            li_packed >>= 3;
+        }
+    }
+
+    // weights, sums in slot order: lane j of a half fetches the score of its
+    // slot's expert from the lane that holds it
+    const int src_lane = (half << 5) + my_e / EPL, src_i = my_e % EPL;
+    float sv = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const float v = __shfl(sc[i], src_lane);
+        if (i == src_i) sv = v;
+    }
+    float z0 = 0.f, z1 = 0.f, x00 = 0.f, x01 = 0.f;
+    if constexpr (!SIGMOID) {
+        x00 = readlane_f(sv, 0);
+        x01 = readlane_f(sv, 32);
+    }
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        const float v0 = readlane_f(sv, j), v1 = readlane_f(sv, 32 + j);
+        const float a0 = SIGMOID ? v0 : expf(v0 - x00), a1 = SIGMOID ? v1 : expf(v1 - x01);
+        z0 = (j == 0) ? a0 : z0 + a0;
+        z1 = (j == 0) ? a1 : z1 + a1;
+    }
+    if (live && hl < K) {
+        const float z = half ? z1 : z0;
+        const float num = SIGMOID ? sv : expf(sv - (half ? x01 : x00));
+        const size_t o = static_cast<size_t>(t) * K + hl;
+        a.topk_idx[o] = my_e;
+        a.topk_w[o] = (num / z) * a.route_scale;
+    }
+}
+
 // Experts per lane: the power of two that fits E into one wave.
 int experts_per_lane(int E)
 {
@@ -463,6 +643,34 @@ TK_EXPORT tk_status tk_route(const float* logits, const float* bias, int32_t T, 
         return fail(TK_ERR_ARG,
                     "tk_route: logits and bias must be 16-byte aligned when E %% 4 == 0 and E > 128");
 
+    const bool half_ok = T >= kHalfMinTokens && E > 128 && E <= 256 && E % 8 == 0 && k <= 8 &&
+                         (opts->n_groups == 1 || (E / opts->n_groups) % 8 == 0);
+    if (opts->renormalize && half_ok && (opts->n_groups == 1 || opts->group_topn <= 2)) {
+        const FastArgs f{logits, bias, topk_idx, topk_w, T, E, opts->n_groups,
+                         opts->topk_groups, opts->group_topn,
+                         opts->n_groups > 1 ? E / opts->n_groups / 8 : 0, opts->route_scale};
+        const int64_t tokens_per_block = 2 * tk::kWavesPerBlock;
+        const dim3 grid(static_cast<unsigned>((static_cast<int64_t>(T) + tokens_per_block - 1) /
+                                              tokens_per_block)),
+            block(tk::kBlock);
+        const bool sig = opts->score == TK_SCORE_SIGMOID;
+        hipError_t e = hipErrorInvalidValue;
+#define TK_ROUTE_HALF(K_)                                                                          \
+    e = sig ? tk::launch(route_half_kernel<K_, true>, grid, block, 0, stream, f)                   \
+            : tk::launch(route_half_kernel<K_, false>, grid, block, 0, stream, f)
+        switch (k) {
+        case 1: TK_ROUTE_HALF(1); break;
+        case 2: TK_ROUTE_HALF(2); break;
+        case 3: TK_ROUTE_HALF(3); break;
+        case 4: TK_ROUTE_HALF(4); break;
+        case 5: TK_ROUTE_HALF(5); break;
+        case 6: TK_ROUTE_HALF(6); break;
+        case 7: TK_ROUTE_HALF(7); break;
+        default: TK_ROUTE_HALF(8); break;   // k == 8
+        }
+#undef TK_ROUTE_HALF
+        return tk::launched(e, "tk_route");
+    }
     if (opts->renormalize && epl <= 4 && (opts->n_groups == 1 || opts->group_topn <= 2)) {
         const FastArgs f{logits, bias, topk_idx, topk_w, T, E, opts->n_groups,
                          opts->topk_groups, opts->group_topn, lpg, opts->route_scale};

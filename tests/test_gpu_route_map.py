@@ -75,6 +75,34 @@ def test_route_group_limited(E, n_groups, topk_groups, group_topn, k):
     _assert_route(logits, None, k, **r)
 
 
+# From T = 12288 on, 128 < E <= 256 takes the two-tokens-per-wave form (odd T
+# leaves the last wave's second half without a token); every group layout it
+# accepts, both score functions, with and without bias.
+@pytest.mark.parametrize("T", [12288, 12289])
+@pytest.mark.parametrize("E,n_groups,topk_groups,group_topn,k,score,with_bias", [
+    (256, 8, 4, 2, 8, 1, True), (256, 8, 4, 2, 8, 1, False), (256, 1, 1, 0, 8, 0, False),
+    (256, 1, 1, 0, 6, 1, True), (192, 3, 2, 2, 7, 1, True), (256, 16, 4, 1, 7, 1, True),
+    (256, 32, 8, 2, 8, 1, False), (136, 1, 1, 0, 3, 0, False), (256, 2, 1, 2, 4, 1, True),
+])
+def test_route_two_tokens_per_wave(T, E, n_groups, topk_groups, group_topn, k, score, with_bias):
+    rng = np.random.default_rng(T + E + 7 * n_groups + k)
+    logits = synth.normal_f32(rng, (T, E))
+    bias = rng.uniform(-0.1, 0.1, E).astype(np.float32) if with_bias else None
+    _assert_route(logits, bias, k, score=score, n_groups=n_groups, topk_groups=topk_groups,
+                  group_topn=group_topn, renormalize=1, route_scale=2.5)
+
+
+def test_route_two_tokens_per_wave_ties():
+    # many equal keys and signed zeros at the large-T form's sizes
+    rng = np.random.default_rng(9)
+    x = rng.integers(-2, 3, (12289, 256)).astype(np.float32)
+    x[rng.random(x.shape) < 0.2] = -0.0
+    _assert_route(x, None, 8, score=1, n_groups=8, topk_groups=4, group_topn=2,
+                  renormalize=1, route_scale=2.5)
+    _assert_route(x, None, 8, score=0, n_groups=1, topk_groups=1, group_topn=0,
+                  renormalize=1, route_scale=1.0)
+
+
 def test_route_ties_and_signed_zero():
     rng = np.random.default_rng(5)
     for E, k in ((16, 4), (256, 8), (64, 32), (32, 32)):
