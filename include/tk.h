@@ -108,7 +108,8 @@ typedef struct tk_route_opts {
 } tk_route_opts;
 
 /*
- * tk_route -- top-k expert gating and scoring, one token per wavefront.
+ * tk_route -- top-k expert gating and scoring, one token per wavefront (two
+ * per wavefront for T >= 12288 with 128 < E <= 256; the results are the same).
  *
  * Per token t (row t of logits):
  *  1. selection key per expert e (fp32):

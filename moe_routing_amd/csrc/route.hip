@@ -1,4 +1,5 @@
-// tk_route: top-k expert gating and scoring, one token per 64-lane wave.
+// tk_route: top-k expert gating and scoring, one token per 64-lane wave (two
+// per wave, one per 32-lane half, for many tokens with 128 < E <= 256).
 //
 // Semantics: the moe/ gating ops of TileKernels ("刚刚！DeepSeek开源高性能GPU算子库
 // TileKernels", item moe/) with the order and tie rule of the gating listing
@@ -12,7 +13,8 @@
 // lane-local scan over EPL keys, a 6-step butterfly max, and a ballot whose
 // lowest set lane is the lowest expert index holding the maximum (experts are
 // laid out in lane order).  Groups of E/n_groups experts are aligned runs of
-// lanes, so group scores use butterflies confined to the run.
+// lanes, so group scores use butterflies confined to the run.  The
+// two-tokens-per-wave form lays each token over half a wave in the same way.
 #include "tk_internal.h"
 
 namespace {
