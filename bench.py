@@ -708,8 +708,13 @@ def main() -> int:
     value = T / (ms_per_step * 1e-3)
     gbps = BYTES["total"] / (ms_per_step * 1e-3) / 1e9
     warm_gbps = BYTES["total"] / (warm_ms * 1e-3) / 1e9
-    red_s = kern_us["reduce"] * 1e-6
-    achieved = BYTES["reduce"] / red_s / 1e9
+    # tk_reduce_dense goes out as launches of one 16-token workgroup per CU
+    # (two of 4096 tokens each on 256 CUs); the roofline is per launch: a
+    # launch's share of the bytes over its share of the call's time
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    red_launches = -(-(-(-T // 16)) // cus)
+    red_s = kern_us["reduce"] * 1e-6 / red_launches
+    achieved = BYTES["reduce"] / red_launches / red_s / 1e9
     traffic = measured_traffic()
     result = {
         "metric": "routed tokens/s and achieved HBM GB/s (% of peak), T=8192 H=7168 E=256 k=8",
@@ -762,7 +767,9 @@ def main() -> int:
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic,
-                     "algorithmic_bytes_per_launch": BYTES["reduce"]},
+                     "algorithmic_bytes_per_launch": BYTES["reduce"] // red_launches,
+                     "launches_per_call": red_launches,
+                     "launch_us": round(kern_us["reduce"] / red_launches, 2)},
         "parity": None,
         "cpu_baseline": None,
         "next_rows": next_rows,

@@ -24,7 +24,17 @@
 // after all of its reads.  With the writes grouped into bursts the HBM bus
 // turns between reads and writes less often: 174-177 -> 169-170 us at
 // T=8192, H=7168, k=8, while the same schedule with each unit stored as soon
-// as it is combined takes 201 us.  When most slots are masked (one GPU's
+// as it is combined takes 201 us.  One such workgroup fits on a CU at a time,
+// so they go out in launches of one per CU, with the tokens spread evenly
+// over the launches (fewer than 16 per workgroup when T is not a multiple of
+// 16 x CUs).  A single launch of all of them leaves the last, partial
+// round to a fraction of the chip and lets workgroups of different
+// rounds overlap their reads and writes; at H=7168, k=8 the launches
+// measured 118 -> 95 us at T=4500, 227 -> 217 us at T=10000, 719 -> 672 us
+// at T=32768 and 1705 -> 1588 us at T=76800 (bit-identical output; 1-3 us
+// at T=8192, where the single launch's rounds are already full).  A
+// device-wide barrier between each launch's reads and its stores added
+// nothing more.  When most slots are masked (one GPU's
 // expert-parallel share: two thirds of the tokens have no local route) the
 // big workgroups lose to the many short waves of tk_reduce (170-190 vs
 // 122-136 us), and the call cannot see the routing, so the caller chooses.
@@ -100,11 +110,11 @@ constexpr int kMaxDevices = 64;
 template <int K>
 __global__ __launch_bounds__(kStThreads) void reduce_staged_kernel(
     const uint16_t* __restrict__ y, int64_t rows_in, const int32_t* __restrict__ pos,
-    const float* __restrict__ w, int T, int H, int chunks, int tpw, uint16_t* __restrict__ out)
+    const float* __restrict__ w, int T, int H, int chunks, int tpw, int g0, uint16_t* __restrict__ out)
 {
     const int lane = threadIdx.x & (tk::kWave - 1);
     const int wave = tk::uniform(threadIdx.x / tk::kWave);
-    const int64_t t_first = static_cast<int64_t>(blockIdx.x) * tpw;
+    const int64_t t_first = (static_cast<int64_t>(g0) + blockIdx.x) * tpw;
     const int64_t left = T - t_first;
     const int nt = left <= 0 ? 0 : (left > tpw ? tpw : static_cast<int>(left));
     const int t0 = nt > 0 ? static_cast<int>(t_first) : 0;
@@ -186,21 +196,31 @@ int device_cus(int dev)
     return n > 0 ? n : 0;
 }
 
-// The staged form when it applies: at least one workgroup of tokens per CU
-// (with fewer the chip idles, and the one-wave-per-unit kernel is faster).
+// The staged form when it applies: at least one full workgroup of tokens per
+// CU (with fewer the chip idles, and the one-wave-per-unit kernel is faster).
+// Only one of these workgroups fits on a CU at a time, so the work goes out as
+// `phases` launches of one workgroup per CU, the tokens spread evenly over
+// them (tpw = ceil(T / (phases * CUs)) <= the cap): every launch fills the chip, and
+// each starts its reads only when the previous one has written all of its rows.
 template <int K>
 bool launch_staged(const uint16_t* y, int64_t rows, const int32_t* pos, const float* w, int T,
                    int H, uint16_t* out, hipStream_t stream, hipError_t* e)
 {
     const int chunks = (H + kChunk - 1) / kChunk;
-    const int tpw = staged_tokens(chunks);
+    const int cap = staged_tokens(chunks);
     int dev = -1;
-    if (tpw == 0 || hipGetDevice(&dev) != hipSuccess) return false;
-    const int cus = device_cus(dev);
-    if (cus == 0 || static_cast<int64_t>(T) < static_cast<int64_t>(cus) * tpw) return false;
-    const int64_t groups = (static_cast<int64_t>(T) + tpw - 1) / tpw;
-    *e = tk::launch(reduce_staged_kernel<K>, dim3(static_cast<unsigned>(groups)), dim3(kStThreads),
-                    0, stream, y, rows, pos, w, T, H, chunks, tpw, out);
+    if (cap == 0 || hipGetDevice(&dev) != hipSuccess) return false;
+    const int64_t cus = device_cus(dev);
+    if (cus == 0 || static_cast<int64_t>(T) < cus * cap) return false;
+    const int64_t phases = ((static_cast<int64_t>(T) + cap - 1) / cap + cus - 1) / cus;
+    const int tpw = static_cast<int>((static_cast<int64_t>(T) + phases * cus - 1) / (phases * cus));
+    const int64_t groups = (static_cast<int64_t>(T) + tpw - 1) / tpw;   // <= phases * cus
+    for (int64_t g0 = 0; g0 < groups; g0 += cus) {
+        const int64_t n = groups - g0 < cus ? groups - g0 : cus;
+        *e = tk::launch(reduce_staged_kernel<K>, dim3(static_cast<unsigned>(n)), dim3(kStThreads),
+                        0, stream, y, rows, pos, w, T, H, chunks, tpw, static_cast<int>(g0), out);
+        if (*e != hipSuccess) break;
+    }
     return true;
 }
 
