@@ -288,7 +288,9 @@ tk_status tk_reduce(const void* y_bf16, int64_t rows, const int32_t* pos, const 
  * tk_reduce_dense -- tk_reduce for dense routings: the same arguments,
  * checks, errors and bit-identical results.  A workgroup combines up to 16
  * consecutive tokens, holds the results in registers and stores their rows
- * as one burst after all of its reads, which pays off when (nearly) every
+ * as one burst after all of its reads; the workgroups go out as several
+ * launches on `stream`, one workgroup per compute unit each, with the tokens
+ * spread evenly over them.  This pays off when (nearly) every
  * slot has a row -- no local-expert mask, as in a single-GPU layer -- and
  * loses to tk_reduce when most slots are masked (one GPU's share of an
  * expert-parallel layer).  It takes tk_reduce's kernel itself for small T
