@@ -376,3 +376,41 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_c_program_uses_the_header_and_library(lib, tmp_path):
+    # include/tk.h is a C header: a C11 program built with -pedantic -Werror
+    # (the ROCm headers taken as system headers) links libtk.so and sees the
+    # same status codes, per-thread messages, size queries and tk_route_opts
+    # layout as the ctypes binding
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no gcc")
+    lib_dir = os.path.join(ROOT, "moe_routing_amd")
+    exe = str(tmp_path / "abi_consumer")
+    subprocess.run([gcc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-pedantic",
+                    "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                    "-isystem", "/opt/rocm/include",
+                    os.path.join(ROOT, "tests", "helpers", "abi_consumer.c"), "-o", exe,
+                    "-L", lib_dir, "-ltk", f"-Wl,-rpath,{lib_dir}"], check=True, timeout=120)
+    out = subprocess.run([exe], capture_output=True, text=True, check=True, timeout=60).stdout
+    got = {}
+    for line in out.splitlines():
+        name, *vals = line.split()
+        got[name] = [int(v) for v in vals]
+    assert got["initial_error_empty"] == [1]
+    assert got["opts_size"] == [ctypes.sizeof(RouteOpts)]
+    assert got["opts_scale_offset"] == [RouteOpts.route_scale.offset]
+    assert got["route_null_opts"] == [ARG, 1]
+    assert got["route_too_many_experts"] == [UNSUP, 1]
+    assert got["reduce_bad_h"] == [ARG, 1]
+    assert got["reduce_no_tokens"] == [0, 0]          # a no-op, and the message cleared
+    assert got["expand_bad_mode"] == [ARG, 1]
+    L = ctypes.c_int32
+    assert got["map_ws"] == [lib.tk_map_workspace_bytes(L(8192), L(8), L(256))]
+    assert got["balance_ws"] == [lib.tk_balance_workspace_bytes(L(8192), L(256))]
+    lib.tk_quant_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
+    pc = int(re.search(r"#define TK_QUANT_FP8_PER_CHANNEL (\d+)", open(HEADER).read()).group(1))
+    assert got["quant_pc_ws"] == [lib.tk_quant_workspace_bytes(8192, 7168, pc)]
