@@ -123,5 +123,30 @@ def build_asan(verbose: bool = False) -> str:
     return ASAN_LIB
 
 
+ABI_PIPELINE_SRC = os.path.join(ROOT, "tests", "helpers", "abi_pipeline.c")
+ABI_PIPELINE = os.path.join(ROOT, "tests", "helpers", "abi_pipeline")
+
+
+def build_abi_pipeline(verbose: bool = False) -> str:
+    """The C program the GPU tests run to drive the routing path through the C
+    ABI alone (tests/helpers/abi_pipeline.c): plain C11 with the host
+    compiler, linked against libtk.so and the HIP runtime, found at run time
+    relative to the program."""
+    rocm = os.path.dirname(os.path.dirname(HIPCC))
+    tmp = ABI_PIPELINE + ".tmp"
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-pedantic",
+           "-D__HIP_PLATFORM_AMD__", "-I", INCLUDE, "-isystem", os.path.join(rocm, "include"),
+           ABI_PIPELINE_SRC, "-o", tmp, "-L", PKG, "-ltk", "-L", os.path.join(rocm, "lib"),
+           "-lamdhip64", "-Wl,-rpath,$ORIGIN/../../moe_routing_amd",
+           f"-Wl,-rpath,{os.path.join(rocm, 'lib')}"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"gcc failed on abi_pipeline.c:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, ABI_PIPELINE)
+    if verbose:
+        print(f"built {ABI_PIPELINE}")
+    return ABI_PIPELINE
+
+
 if __name__ == "__main__":
     build(verbose=True)
