@@ -288,14 +288,15 @@ tk_status tk_reduce(const void* y_bf16, int64_t rows, const int32_t* pos, const 
  * tk_reduce_dense -- tk_reduce for dense routings: the same arguments,
  * checks, errors and bit-identical results.  A workgroup combines up to 16
  * consecutive tokens, holds the results in registers and stores their rows
- * as one burst after all of its reads; the workgroups go out as several
- * launches on `stream`, one workgroup per compute unit each, with the tokens
- * spread evenly over them.  This pays off when (nearly) every
+ * as one burst after all of its reads; the workgroups run in rounds of one
+ * per compute unit with the tokens spread evenly over them, and for large
+ * rows (a round of at least 480 MiB) each round is a launch of its own on
+ * `stream`.  This pays off when (nearly) every
  * slot has a row -- no local-expert mask, as in a single-GPU layer -- and
  * loses to tk_reduce when most slots are masked (one GPU's share of an
  * expert-parallel layer).  It takes tk_reduce's kernel itself for small T
- * (fewer than one workgroup of tokens per compute unit), runtime k (k not in
- * {1, 2, 4, 6, 8}) and H > 114688.
+ * (fewer than one workgroup of tokens per compute unit), short rows
+ * (H <= 1536), runtime k (k not in {1, 2, 4, 6, 8}) and H > 114688.
  */
 tk_status tk_reduce_dense(const void* y_bf16, int64_t rows, const int32_t* pos,
                           const float* topk_w, int32_t T, int32_t k, int32_t H, void* out_bf16,

@@ -25,16 +25,18 @@
 // turns between reads and writes less often: 174-177 -> 169-170 us at
 // T=8192, H=7168, k=8, while the same schedule with each unit stored as soon
 // as it is combined takes 201 us.  One such workgroup fits on a CU at a time,
-// so they go out in launches of one per CU, with the tokens spread evenly
-// over the launches (fewer than 16 per workgroup when T is not a multiple of
-// 16 x CUs).  A single launch of all of them leaves the last, partial
-// round to a fraction of the chip and lets workgroups of different
-// rounds overlap their reads and writes; at H=7168, k=8 the launches
-// measured 118 -> 95 us at T=4500, 227 -> 217 us at T=10000, 719 -> 672 us
-// at T=32768 and 1705 -> 1588 us at T=76800 (bit-identical output; 1-3 us
-// at T=8192, where the single launch's rounds are already full).  A
-// device-wide barrier between each launch's reads and its stores added
-// nothing more.  When most slots are masked (one GPU's
+// so they run in rounds of one per CU, with the tokens spread evenly over the
+// rounds (fewer than 16 per workgroup when T is not a multiple of 16 x CUs):
+// with 16 each, T=4500 left its second round a quarter full (122 -> 98 us at
+// H=7168, k=8).  Where a round moves at least 480 MiB (H=7168, k=8: 504 MiB
+// on 256 CUs) each round is a launch of its own, so that all workgroups work
+// on one window of consecutive tokens at a time: 728 -> 703 us at T=32768
+// and 1705 -> 1588 us at T=76800, the same within noise up to T=16384; with
+// smaller rounds the launch boundaries cost more than the windows give (4 to
+// 49 launches of 9-453 MB: up to 40 % slower).  Rows shorter than four
+// 512-column units take tk_reduce's kernel (H=256: 124 against 90 us; even
+// at H=2048).  A device-wide barrier between each launch's reads and its
+// stores added nothing.  When most slots are masked (one GPU's
 // expert-parallel share: two thirds of the tokens have no local route) the
 // big workgroups lose to the many short waves of tk_reduce (170-190 vs
 // 122-136 us), and the call cannot see the routing, so the caller chooses.
@@ -105,6 +107,8 @@ constexpr int kStThreads = 1024;                       // 16 waves per workgroup
 constexpr int kStWaves = kStThreads / tk::kWave;
 constexpr int kStUnits = 14;                           // units per wave at most
 constexpr int kStMaxTokens = 16;                       // tokens per workgroup at most
+constexpr int kStMinChunks = 4;                        // staged form from H > 1536 on
+constexpr int64_t kStRoundBytes = int64_t(480) << 20;  // one launch per round from here on
 constexpr int kMaxDevices = 64;
 
 template <int K>
@@ -196,12 +200,17 @@ int device_cus(int dev)
     return n > 0 ? n : 0;
 }
 
-// The staged form when it applies: at least one full workgroup of tokens per
-// CU (with fewer the chip idles, and the one-wave-per-unit kernel is faster).
-// Only one of these workgroups fits on a CU at a time, so the work goes out as
-// `phases` launches of one workgroup per CU, the tokens spread evenly over
-// them (tpw = ceil(T / (phases * CUs)) <= the cap): every launch fills the chip, and
-// each starts its reads only when the previous one has written all of its rows.
+// The staged form when it applies: rows of at least kStMinChunks units (with
+// shorter rows a workgroup holds little work, and the many small workgroups
+// of the one-wave-per-unit kernel hide latency better) and at least one full
+// workgroup of tokens per CU (with fewer the chip idles).  Only one of these
+// workgroups fits on a CU at a time, so they run in rounds of one per CU; the
+// tokens are spread evenly over the rounds (tpw = ceil(T / (rounds * CUs)) <=
+// the cap), so that the last round is as full as the others.  When a full
+// round moves at least kStRoundBytes, each round is a launch of its own: every
+// workgroup of a launch works on one window of consecutive tokens, whose
+// rows (expert-contiguous, in token order within each expert) lie in short
+// runs, and the next window starts only after the previous one is written.
 template <int K>
 bool launch_staged(const uint16_t* y, int64_t rows, const int32_t* pos, const float* w, int T,
                    int H, uint16_t* out, hipStream_t stream, hipError_t* e)
@@ -209,14 +218,16 @@ bool launch_staged(const uint16_t* y, int64_t rows, const int32_t* pos, const fl
     const int chunks = (H + kChunk - 1) / kChunk;
     const int cap = staged_tokens(chunks);
     int dev = -1;
-    if (cap == 0 || hipGetDevice(&dev) != hipSuccess) return false;
+    if (cap == 0 || chunks < kStMinChunks || hipGetDevice(&dev) != hipSuccess) return false;
     const int64_t cus = device_cus(dev);
     if (cus == 0 || static_cast<int64_t>(T) < cus * cap) return false;
-    const int64_t phases = ((static_cast<int64_t>(T) + cap - 1) / cap + cus - 1) / cus;
-    const int tpw = static_cast<int>((static_cast<int64_t>(T) + phases * cus - 1) / (phases * cus));
-    const int64_t groups = (static_cast<int64_t>(T) + tpw - 1) / tpw;   // <= phases * cus
-    for (int64_t g0 = 0; g0 < groups; g0 += cus) {
-        const int64_t n = groups - g0 < cus ? groups - g0 : cus;
+    const int64_t rounds = ((static_cast<int64_t>(T) + cap - 1) / cap + cus - 1) / cus;
+    const int tpw = static_cast<int>((static_cast<int64_t>(T) + rounds * cus - 1) / (rounds * cus));
+    const int64_t groups = (static_cast<int64_t>(T) + tpw - 1) / tpw;   // <= rounds * cus
+    const int64_t token_bytes = (static_cast<int64_t>(K) * 2 + 2) * H + static_cast<int64_t>(K) * 8;
+    const int64_t per_launch = cus * cap * token_bytes >= kStRoundBytes ? cus : groups;
+    for (int64_t g0 = 0; g0 < groups; g0 += per_launch) {
+        const int64_t n = groups - g0 < per_launch ? groups - g0 : per_launch;
         *e = tk::launch(reduce_staged_kernel<K>, dim3(static_cast<unsigned>(n)), dim3(kStThreads),
                         0, stream, y, rows, pos, w, T, H, chunks, tpw, static_cast<int>(g0), out);
         if (*e != hipSuccess) break;

@@ -8,9 +8,10 @@ positions, row sources, codes and scales bit for bit, weights within the
 weight tolerance, the combine within the combine tolerance.
 
 Cases: the DeepSeek-V3 gating (sigmoid + bias, 8 groups, top-4 groups,
-x2.5) at T=1000 with tk_reduce and at T=4500 with tk_reduce_dense (its
-staged form in two launches); a masked share (softmax, experts [16, 40) of
-64 local, k=6) at T=777; and the tiny softmax top-2 configuration.
+x2.5) at T=1000, H=1024 with tk_reduce and at T=4500, H=2048 with
+tk_reduce_dense (its staged form: two rounds of 9-token workgroups); a masked
+share (softmax, experts [16, 40) of 64 local, k=6) at T=777; and the tiny
+softmax top-2 configuration.
 """
 import os
 import subprocess
@@ -32,7 +33,7 @@ SOFTMAX, SIGMOID = 0, 1
 CASES = {
     "v3_T1000": dict(T=1000, E=256, k=8, H=1024, route=synth.ROUTE_V3, bias=True, local=None,
                      dense=0),
-    "v3_T4500_dense": dict(T=4500, E=256, k=8, H=1024, route=synth.ROUTE_V3, bias=True,
+    "v3_T4500_dense": dict(T=4500, E=256, k=8, H=2048, route=synth.ROUTE_V3, bias=True,
                            local=None, dense=1),
     "masked_softmax": dict(T=777, E=64, k=6, H=512, local=(16, 40), bias=False, dense=0,
                            route=dict(score=SOFTMAX, n_groups=1, topk_groups=1, group_topn=0,

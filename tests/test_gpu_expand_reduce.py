@@ -226,22 +226,25 @@ def test_reduce_few_tokens(T, k):
     _check_reduce(y, pos, w)
 
 
-# tk_reduce_dense: at T >= (compute units) x (tokens per workgroup, 16 here) it
-# takes its staged form (a workgroup combines up to 16 consecutive tokens,
-# keeps the results in registers and stores its rows as one burst after a
-# barrier), in launches of one workgroup per CU with the tokens spread evenly
-# over them (on 256 CUs: T=4100 -> 9 tokens per workgroup, launches of 256 and
-# 200; T=10000 -> 14, 256+256+203; T=12289 -> 13, 256+256+256+178);
-# tk_reduce, slices of 1000 tokens and T just below the threshold take the
-# one-wave-per-unit kernel.  Per token the arithmetic is the same, so all must
-# agree bit for bit; both stay within the combine tolerance of the oracle.
-# Cases: every compiled k, ragged last workgroups and launches, a 520-column
-# row (a partly filled 512-column unit), masked slots and rows beyond y.
+# tk_reduce_dense: for rows of at least four 512-column units and T >=
+# (compute units) x 16 it takes its staged form (a workgroup combines up to 16
+# consecutive tokens, keeps the results in registers and stores its rows as
+# one burst after a barrier), in rounds of one workgroup per CU with the
+# tokens spread evenly over them (on 256 CUs: T=4500 -> 9 tokens per
+# workgroup, 256 + 244 workgroups; T=5333 -> 11, 256 + 229), one launch per
+# round when a round moves at least 480 MiB (k=8, H=7168: T=8191 -> 16
+# tokens, launches of 256 + 256 workgroups, the last one short a token;
+# T=9000 -> 12 tokens, 256 + 256 + 238); shorter rows, tk_reduce, slices of
+# 1000 tokens and T just below the threshold take the one-wave-per-unit
+# kernel.  Per token the arithmetic is the same, so all must agree bit for
+# bit; both stay within the combine tolerance of the oracle.  Cases: every
+# compiled k, ragged last workgroups, rounds and launches, a 520-column row
+# (a partly filled 512-column unit), masked slots and rows beyond y.
 @pytest.mark.parametrize("T,k,H", [(4096, 8, 7168), (4100, 8, 1024), (5000, 6, 2048),
-                                   (4500, 4, 4096), (4600, 2, 520), (4097, 1, 1024),
+                                   (4500, 4, 4096), (4600, 2, 520), (4097, 1, 2048),
                                    (4111, 6, 7168), (5333, 4, 7168), (4095, 8, 7168),
-                                   (4500, 8, 4096), (10000, 8, 1024), (12289, 4, 520),
-                                   (8191, 8, 7168),
+                                   (4500, 8, 4096), (10000, 8, 1024), (12289, 4, 3072),
+                                   (8191, 8, 7168), (9000, 8, 7168), (4400, 2, 2056),
                                    # runtime k: the one-wave-per-unit kernel for both
                                    (4096, 12, 1024), (4200, 32, 520)])
 def test_reduce_dense_equals_reduce(T, k, H):
