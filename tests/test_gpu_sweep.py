@@ -79,3 +79,53 @@ def test_path_sweep(seed):
     got = tk.tk_reduce(to_dev(y, bf16=True), pos, w)
     rep = combine_report(to_host(got), oracle.reduce(y, op, o_w.astype(np.float32)))
     assert rep["ok"], rep
+
+
+# tk_reduce_dense around its thresholds: rows of H = 1536 (the one-wave-per-unit
+# kernel) and longer (the staged form), partly filled 512-column units, every
+# compiled k, T from just below to a few rounds above (compute units) x 16
+# tokens, and k = 8 with H = 7168 (one launch per round).  Positions are a
+# routing from the oracle's map of random expert choices (expert-contiguous
+# rows, as tk_map lays them out), with a few slots masked; y is drawn on the
+# device.  The dense combine must equal tk_reduce bit for bit on every token,
+# and sampled tokens (first, last, random) are compared with the oracle.
+DENSE_H = [1536, 1544, 2048, 2056, 2568, 3072, 4096, 5120, 6144, 7168]
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_reduce_dense_sweep(seed):
+    import torch
+    rng = np.random.default_rng(1000 + seed)
+    k = int(rng.choice([1, 2, 4, 6, 8]))
+    H = 7168 if seed % 4 == 0 else int(rng.choice(DENSE_H))
+    if seed % 4 == 0:
+        k = 8
+    E = 256
+    T_max = max(4200, min(16000, (300 << 20) // (k * H)))
+    T = int(rng.integers(3800, T_max + 1))
+    R = T * k
+    idx = synth.random_routing(rng, T, E, k)
+    _, _, pos, _ = oracle.map_routes(idx, E)
+    pos = pos.copy()
+    pos[rng.random((T, k)) < 0.05] = -1
+    w = rng.uniform(0.05, 0.6, (T, k)).astype(np.float32)
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    y = torch.randn((R, H), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    pd, wd = to_dev(pos), to_dev(w)
+    dense = tk.tk_reduce_dense(y, pd, wd)
+    plain = tk.tk_reduce(y, pd, wd)
+    torch.cuda.synchronize()
+    print(f"dense sweep seed {seed}: T={T} k={k} H={H}", flush=True)
+    assert torch.equal(dense, plain), "tk_reduce_dense differs from tk_reduce"
+    sample = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 40, replace=False)]))
+    rows = pos[sample]
+    used = rows[rows >= 0]
+    y_s = to_host(y[torch.from_numpy(used.astype(np.int64)).to(dev)])
+    # the sampled tokens' rows renumbered 0.. in order, masked slots kept masked
+    pos_s = np.full(rows.shape, -1, np.int32)
+    pos_s[rows >= 0] = np.arange(used.size, dtype=np.int32)
+    rep = combine_report(to_host(dense[torch.from_numpy(sample).to(dev)]),
+                         oracle.reduce(y_s, pos_s, w[sample]))
+    assert rep["ok"], rep
