@@ -61,7 +61,7 @@ def _same(a, b):
     return all(torch.equal(u, v) for u, v in zip(a, b))
 
 
-# both combines: at T=4096, H=2048 tk_reduce_dense takes its staged form (16 tokens per workgroup)
+# both combines: at T=4096, H=2048 tk_reduce_dense takes its staged form (16 tokens per workgroup, one launch)
 @pytest.mark.parametrize("reduce", ["tk_reduce", "tk_reduce_dense"])
 def test_step_replays_from_a_graph(reduce):
     dev = torch.device("cuda:0")
@@ -113,3 +113,38 @@ def test_two_steps_on_concurrent_streams(reduce):
     torch.cuda.synchronize()
     assert _same(a.outputs(), ref_a)
     assert _same(b.outputs(), ref_b)
+
+
+def test_dense_combine_in_launches_replays_from_a_graph():
+    # k=8, H=7168: tk_reduce_dense issues one launch per round of workgroups;
+    # T=9000 -> three launches (256 + 256 + 238 workgroups of 12 tokens), all
+    # captured in the graph and replayed in order
+    dev = torch.device("cuda:0")
+    t9, h9 = 9000, 7168
+    g = torch.Generator(device=dev)
+    g.manual_seed(9)
+    y = torch.randn((t9 * K, h9), generator=g, device=dev).to(torch.bfloat16)
+    pos = torch.randperm(t9 * K, generator=g, device=dev).to(torch.int32).view(t9, K)
+    w = torch.rand((t9, K), generator=g, device=dev)
+    out = torch.empty((t9, h9), dtype=torch.bfloat16, device=dev)
+    tk.tk_reduce_dense(y, pos, w, out)
+    torch.cuda.synchronize()
+    ref = out.clone()
+    other = Step(5, dev, "tk_reduce_dense")
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        tk.tk_reduce_dense(y, pos, w, out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        tk.tk_reduce_dense(y, pos, w, out)
+    for replay in range(3):
+        out.zero_()
+        other.run()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {replay} differs from the eager call"
