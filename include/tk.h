@@ -133,7 +133,11 @@ typedef struct tk_route_opts {
  *                times route_scale when renormalize == 0.
  *
  * logits   device, fp32 (T, E), 4-byte aligned; 16-byte aligned when E > 128
- *          and E % 4 == 0 (four experts per lane, read as one vector load)
+ *          and E % 4 == 0 (four experts per lane, read as one vector load).
+ *          Finite values: for a token with a NaN or infinite logit the
+ *          experts and weights are unspecified (a NaN may win or lose any
+ *          comparison, and an expert may repeat), but every index written is
+ *          in [0, E), so the map, expand and combine stay within their buffers
  * bias     device, fp32 (E) or NULL; sigmoid only; aligned as logits
  * T        tokens, >= 0
  * E        experts, 1..TK_MAX_EXPERTS

@@ -125,6 +125,44 @@ def test_route_extreme_logits():
                   renormalize=1, route_scale=2.5)
 
 
+def test_route_non_finite_logits_stay_in_range():
+    # non-finite logits are outside the contract (experts and weights
+    # unspecified, an expert may repeat), but every index is an expert id,
+    # and the map still gives each routed slot (the first occurrence of an
+    # id in its token) a distinct row: the routed positions are exactly
+    # 0 .. R-1 and row_src[pos[t, j]] == t
+    for T in (300, 12288):     # one token per wave; two per wave from T = 12288
+        _non_finite_case(np.random.default_rng(16), T)
+
+
+def _non_finite_case(rng, T):
+    E, k = 256, 8
+    x = synth.normal_f32(rng, (T, E))
+    bad = rng.random((T, E)) < 0.05
+    specials = np.array([np.nan, np.inf, -np.inf], np.float32)
+    x[bad] = specials[rng.integers(0, 3, int(bad.sum()))]
+    x[:4] = np.nan                                   # whole rows of NaN
+    x.view(np.uint32)[4:8] = 0xFFFFFFFF              # NaN with every bit set
+    x[8] = np.inf
+    x[9] = -np.inf
+    for score, groups in ((1, (8, 4, 2)), (0, (1, 1, 0)), (1, (1, 1, 0))):
+        r = dict(score=score, n_groups=groups[0], topk_groups=groups[1], group_topn=groups[2],
+                 renormalize=1, route_scale=2.5)
+        idx, w = tk.tk_route(to_dev(x), None, k, tk.RouteOpts(**r))
+        counts, offsets, pos, row_src = tk.tk_map(idx, E)
+        torch.cuda.synchronize()
+        g_idx, g_pos, g_rs = to_host(idx), to_host(pos), to_host(row_src)
+        assert ((g_idx >= 0) & (g_idx < E)).all(), "an index outside [0, E)"
+        R = int(to_host(offsets)[-1])
+        routed = g_pos >= 0
+        earlier = (g_idx[:, :, None] == g_idx[:, None, :]) & np.tri(k, k, -1, dtype=bool)[None]
+        first = ~earlier.any(2)
+        assert np.array_equal(routed, first)
+        assert np.array_equal(np.sort(g_pos[routed]), np.arange(R))
+        tok = np.repeat(np.arange(T), k).reshape(T, k)
+        assert np.array_equal(g_rs[g_pos[routed]], tok[routed])
+
+
 def test_route_zero_tokens():
     opts = tk.RouteOpts(score=1)
     idx, w = tk.tk_route(torch.empty((0, 64), device="cuda"), None, 4, opts)
