@@ -253,6 +253,9 @@ tk_status tk_map_noalloc(const int32_t* topk_idx, int32_t T, int32_t k, int32_t 
  *   amax = max(max |x|, 1e-4), scale = RN32(amax / 448),
  *   q = E4M3(RN32(x / scale)) -- OCP E4M3FN, round to nearest even, sign kept;
  *   scales[row, b] = scale for every row of the token.
+ * The FP8 mode assumes finite x: a block holding a NaN or an infinity gets
+ * unspecified codes and scale (the bf16 mode copies any bits).  Where the
+ * rows go never depends on the values.
  *
  * x_bf16        device, bf16 (T, H), 16-byte aligned
  * T, H, k       T >= 0; H > 0 with H % 8 == 0 (bf16) or H % 128 == 0 (FP8)
