@@ -440,7 +440,8 @@ tk_status tk_balance_loss(const float* logits, const int32_t* topk_idx, int32_t 
  * then per 128-column block: amax = max(max |a|, 1e-4), scale = RN(amax/448),
  * out[r, c] = E4M3(RN(a / scale)) (OCP E4M3FN, nearest even, sign kept),
  * scales[r, c/128] = scale.  Rows r >= n are not written.
- * Activations that overflow fp32 (|g*u| beyond ~3.4e38) give unspecified codes.
+ * A NaN or infinite h, or an activation that overflows fp32 (|g*u| beyond
+ * ~3.4e38), gives its block unspecified codes and scale.
  * Weighted when row_src, pos and topk_w are all given (all NULL: unweighted):
  * w_r = topk_w[t, j] for t = row_src[r] and the slot j with pos[t, j] == r
  * (as written by tk_map), 0 if there is none.
