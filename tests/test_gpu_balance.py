@@ -34,7 +34,8 @@ def _check(logits, idx, score):
 
 @pytest.mark.parametrize("score", [tk.TK_SCORE_SIGMOID, tk.TK_SCORE_SOFTMAX])
 @pytest.mark.parametrize("T,E,k", [(1, 8, 1), (33, 16, 2), (300, 100, 6), (513, 256, 8),
-                                   (64, 1024, 32), (100, 5, 5), (4000, 64, 4)])
+                                   (64, 1024, 32), (100, 5, 5), (4000, 64, 4),
+                                   (70001, 256, 8)])   # 2188 tiles: many final-pass batches
 def test_balance_random(T, E, k, score):
     rng = np.random.default_rng(T * 7 + E + k + score)
     logits = synth.normal_f32(rng, (T, E))

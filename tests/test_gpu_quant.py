@@ -42,7 +42,8 @@ def _check(x, mode):
 
 
 @pytest.mark.parametrize("mode", MODES)
-@pytest.mark.parametrize("rows,cols", [(1, 128), (37, 384), (130, 1152), (300, 2048), (5, 7168)])
+@pytest.mark.parametrize("rows,cols", [(1, 128), (37, 384), (130, 1152), (300, 2048), (5, 7168),
+                                       (2, 65536), (129, 16384), (3000, 128)])
 def test_quant_random(mode, rows, cols):
     _check(_matrix(np.random.default_rng(rows * 31 + cols + mode), rows, cols), mode)
 
