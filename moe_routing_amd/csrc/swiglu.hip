@@ -123,6 +123,7 @@ __device__ __forceinline__ float pick_weight(const SwigluArgs& a, int t, int lan
 constexpr int kSThreads = 512;                 // 8 waves per workgroup
 constexpr int kSWaves = kSThreads / tk::kWave;
 constexpr int kSBlocks = 1024;                 // 4 per CU of a 256-CU device
+constexpr int kSStageScales = 64;              // scales per row gathered in LDS (I <= 8192)
 
 template <bool WEIGHTED>
 __global__ __launch_bounds__(kSThreads) void swiglu_quant_kernel(SwigluArgs a)
@@ -141,7 +142,16 @@ __global__ __launch_bounds__(kSThreads) void swiglu_quant_kernel(SwigluArgs a)
     // r + 2 * stride does not wrap
     const uint32_t rows = static_cast<uint32_t>(rows64);
     const uint32_t stride = gridDim.x * kSWaves;
-    uint32_t r = blockIdx.x * kSWaves + tk::uniform(threadIdx.x / tk::kWave);
+    const int wave = tk::uniform(threadIdx.x / tk::kWave);
+    uint32_t r = blockIdx.x * kSWaves + wave;
+    // A workgroup's waves take 8 adjacent rows per iteration, so their scales
+    // (I/128 per row; 64 bytes at I = 2048) share cache lines: when a row has
+    // at most kSStageScales of them they are gathered in LDS and leave as
+    // whole lines after the iteration, instead of as 32-byte pieces from
+    // different waves (1-1.5 us of about 127).
+    __shared__ float sc_stage[kSWaves * kSStageScales];
+    const int nbr = a.I / 128;
+    const bool stage_sc = nbr <= kSStageScales;
 
     // Routing weights run ahead of the rows: while row r is processed, the
     // token of row r + 2*stride and the slots of row r + stride's token are
@@ -153,7 +163,10 @@ __global__ __launch_bounds__(kSThreads) void swiglu_quant_kernel(SwigluArgs a)
         w = pick_weight(a, t0, lane, r);
         t1 = r + stride < rows ? a.row_src[r + stride] : -1;
     }
-    for (; r < rows; r += stride) {
+    // the loop runs while the workgroup's first row is in range (uniform, as
+    // the barriers need); a wave past the last row only takes the barriers
+    for (uint32_t base = blockIdx.x * kSWaves; base < rows; base += stride, r += stride) {
+        const bool live = r < rows;
         int t2 = -1;
         int32_t p1 = -1;
         float w1 = 0.0f;
@@ -167,7 +180,7 @@ __global__ __launch_bounds__(kSThreads) void swiglu_quant_kernel(SwigluArgs a)
         const uint16_t* hr = a.h + static_cast<size_t>(r) * 2 * a.I;
         uint8_t* orow = a.out + static_cast<size_t>(r) * a.I;
         float* srow = a.scales + static_cast<size_t>(r) * (a.I / 128);
-        for (int col0 = 0; col0 < a.I; col0 += kChunk) {
+        for (int col0 = 0; live && col0 < a.I; col0 += kChunk) {
             const int col = col0 + lane * 16;
             const bool active = col < a.I;   // I % 128 == 0: 8-lane groups are wholly in or out
             tk::u32x4 g0 = tk::u32x4{0u, 0u, 0u, 0u}, g1 = g0, u0 = g0, u1 = g0;
@@ -208,8 +221,20 @@ __global__ __launch_bounds__(kSThreads) void swiglu_quant_kernel(SwigluArgs a)
                                  tk::fp8_quotient(v[14], scale, inv), tk::fp8_quotient(v[15], scale, inv));
             if (active) {
                 tk::store_stream(orow + col, q);
-                if ((lane & 7) == 0) srow[col / 128] = scale;
+                if ((lane & 7) == 0) {
+                    if (stage_sc) sc_stage[wave * kSStageScales + col / 128] = scale;
+                    else srow[col / 128] = scale;
+                }
             }
+        }
+        if (stage_sc) {
+            __syncthreads();   // the iteration's rows' scales staged
+            const uint32_t nr = rows - base < kSWaves ? rows - base : kSWaves;
+            for (int i = threadIdx.x; i < static_cast<int>(nr) * nbr; i += kSThreads) {
+                const int rr = i / nbr;
+                a.scales[static_cast<size_t>(base) * nbr + i] = sc_stage[rr * kSStageScales + i - rr * nbr];
+            }
+            __syncthreads();   // read out before the next iteration stages
         }
         if constexpr (WEIGHTED) {
             w = select_weight(p1, w1, r + stride);

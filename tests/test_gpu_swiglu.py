@@ -39,7 +39,10 @@ def _check(h, I, got_q, got_s, rows, row_w=None):
     assert bad.size == 0, f"{bad.size} rows differ, first {bad[:5]}"
 
 
-@pytest.mark.parametrize("R,I", [(64, 128), (100, 384), (257, 1152), (512, 2048), (33, 7168)])
+@pytest.mark.parametrize("R,I", [(64, 128), (100, 384), (257, 1152), (512, 2048), (33, 7168),
+                                 # 64 scales per row (the most gathered in LDS), 65 and 128
+                                 # (stored directly)
+                                 (40, 8192), (21, 8320), (9, 16384)])
 def test_swiglu_quant_random(R, I):
     rng = np.random.default_rng(R + I)
     h = _rows(rng, R, I)
