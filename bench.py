@@ -40,6 +40,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -71,10 +72,14 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_counters_v3_T8192.md")
 
 
 def kernel_source_hash() -> str:
+    """Hash of the combine's code (reduce.hip, tk_internal.h) with comments and
+    whitespace removed, so that an edit of comments alone keeps the counters."""
     h = hashlib.sha256()
     for f in ("reduce.hip", "tk_internal.h"):
-        with open(os.path.join(ROOT, "moe_routing_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "moe_routing_amd", "csrc", f)) as fh:
+            code = re.sub(r"/\*.*?\*/", " ", fh.read(), flags=re.S)
+        code = re.sub(r"//[^\n]*", " ", code)
+        h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -34,8 +34,9 @@
 // and 1705 -> 1588 us at T=76800, the same within noise up to T=16384; with
 // smaller rounds the launch boundaries cost more than the windows give (4 to
 // 49 launches of 9-453 MB: up to 40 % slower).  Rows shorter than four
-// 512-column units take tk_reduce's kernel (H=256: 124 against 90 us; even
-// at H=2048).  A device-wide barrier between each launch's reads and its
+// 512-column units take tk_reduce's kernel (H=256: 124 against 90 us,
+// H=1024: 192 against 185; from H=2048 on the staged form is as fast or
+// faster).  A device-wide barrier between each launch's reads and its
 // stores added nothing.  When most slots are masked (one GPU's
 // expert-parallel share: two thirds of the tokens have no local route) the
 // big workgroups lose to the many short waves of tk_reduce (170-190 vs
