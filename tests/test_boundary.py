@@ -414,3 +414,13 @@ def test_c_program_uses_the_header_and_library(lib, tmp_path):
     lib.tk_quant_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
     pc = int(re.search(r"#define TK_QUANT_FP8_PER_CHANNEL (\d+)", open(HEADER).read()).group(1))
     assert got["quant_pc_ws"] == [lib.tk_quant_workspace_bytes(8192, 7168, pc)]
+
+
+def test_recorded_combine_traffic_matches_its_code():
+    # bench.py reports the combine's measured HBM traffic only while the
+    # committed counter summary was taken on the combine's current code
+    import sys
+    sys.path.insert(0, ROOT)
+    import bench
+    assert bench.measured_traffic() is not None, (
+        "profiles/hbm_counters_v3_T8192.md was taken on other combine code: re-collect it")
