@@ -9,7 +9,8 @@ One step = the whole path over one batch of the DeepSeek-V3-shaped workload
   tk_map           counts, offsets, stable positions (no mask: all local)
   tk_expand_quant  1x128 FP8 E4M3 expand into 65536 expert-contiguous rows
   tk_reduce_dense  bf16 combine of 65536 expert-output rows, fp32 accumulate
-                   (tk_reduce's dense form: every slot has a row here)
+                   (tk_reduce's dense form: every slot has a row here; two
+                   launches of 4096 tokens on 256 compute units)
 
 Inputs are synthetic (seeded normal logits, U(-0.1,0.1) bias, bf16 N(0,1)
 hidden states with 1 % outlier rows x50, bf16 N(0,1) expert outputs) and
@@ -22,11 +23,10 @@ algorithmic HBM GB/s, the same passes back to back (warm: x then stays in the
 MALL), per-kernel times from HIP events recorded between the calls (mean,
 median, p10, p90; warm and cold), the rate of the repository's streaming copy
 kernel for reference (stream_copy), the roofline of the dominant kernel (the
-reduce), the CPU oracle's rate (one thread, and all host cores on token
+reduce, per launch), the CPU oracle's rate (one thread, and all host cores on token
 shards) and the comparison of the step's GPU outputs with the oracle's
 outputs for the same inputs (parity; a mismatch makes the exit status 1).
-Steps beyond the
-routing path (next_rows) are timed separately on the same data and do not
+Steps beyond the routing path (next_rows) are timed separately on the same data and do not
 enter value: SwiGLU + 1x128 FP8 quantisation of the 65536 expanded rows at
 the DeepSeek-V3 expert width I = 2048 (plain and transposing), weighted by the
 routing weights through the step's map; the padded map; the balance loss;
