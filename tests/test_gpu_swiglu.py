@@ -40,6 +40,8 @@ def _check(h, I, got_q, got_s, rows, row_w=None):
 
 
 @pytest.mark.parametrize("R,I", [(64, 128), (100, 384), (257, 1152), (512, 2048), (33, 7168),
+                                 # fewer rows than a workgroup's eight: one partial iteration
+                                 (1, 128), (3, 2048), (7, 7168),
                                  # 64 scales per row (the most gathered in LDS), 65 and 128
                                  # (stored directly)
                                  (40, 8192), (21, 8320), (9, 16384)])
