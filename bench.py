@@ -713,11 +713,14 @@ def main() -> int:
     value = T / (ms_per_step * 1e-3)
     gbps = BYTES["total"] / (ms_per_step * 1e-3) / 1e9
     warm_gbps = BYTES["total"] / (warm_ms * 1e-3) / 1e9
-    # tk_reduce_dense goes out as launches of one 16-token workgroup per CU
-    # (two of 4096 tokens each on 256 CUs); the roofline is per launch: a
+    # tk_reduce_dense runs rounds of one 16-token workgroup per CU, each round
+    # a launch of its own when a round moves at least 480 MiB (at this shape
+    # on 256 CUs: two launches of 4096 tokens); the roofline is per launch: a
     # launch's share of the bytes over its share of the call's time
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    red_launches = -(-(-(-T // 16)) // cus)
+    rounds = -(-(-(-T // 16)) // cus)
+    round_bytes = cus * 16 * ((2 * K + 2) * H + 8 * K)
+    red_launches = rounds if round_bytes >= (480 << 20) else 1
     red_s = kern_us["reduce"] * 1e-6 / red_launches
     achieved = BYTES["reduce"] / red_launches / red_s / 1e9
     traffic = measured_traffic()
