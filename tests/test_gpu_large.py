@@ -114,6 +114,10 @@ def test_large_combine(big, fn):
     w = big["rng"].uniform(0.05, 0.6, (T, K)).astype(np.float32)
     out = getattr(tk, fn)(y, to_dev(opos), to_dev(w))
     torch.cuda.synchronize()
+    if fn == "tk_reduce_dense":
+        # every token against the one-wave-per-unit kernel (the same arithmetic;
+        # here the dense form runs 19 launches of 256 workgroups)
+        assert torch.equal(out, tk.tk_reduce(y, to_dev(opos), to_dev(w))), "dense != plain"
     # the sampled tokens' rows, renumbered 0.. for the oracle
     rows = opos[sample].reshape(-1)
     y_s = _bits(y[torch.from_numpy(rows.astype(np.int64)).to(dev)])
